@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against facts fixed outside it: published test
+vectors, closed forms, library routines and brute force on tiny inputs.
+
+Each test would fail on a plausible mistake in the oracle: a wrong sign
+placement (signs after vs before H), a transposed R, a dropped 1/sqrt(g), a
+wrong rounding mode or order, an off-by-one in the exponent bound of the
+exact route, a mis-scaled dequant.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SEED = synth.ROT_SEED
+GS = (4, 16, 64, 256)
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split("#")[0].strip() for ln in f if ln.split("#")[0].strip()]
+
+
+# --------------------------------------------------------------------------
+# P1: rotation matrix, signs
+# --------------------------------------------------------------------------
+
+def test_splitmix64_published_outputs():
+    want = [int(v, 16) for v in _golden_lines("splitmix64_seed0.txt")]
+    assert o.splitmix64(0, len(want)) == want
+
+
+def test_hadamard_golden_and_closed_form():
+    h4 = np.array([[int(t) for t in ln.split()] for ln in _golden_lines("hadamard4.txt")])
+    assert np.array_equal(o.hadamard(4), h4)
+    for g in GS:
+        h = o.hadamard(g)
+        i = np.arange(g)
+        par = np.vectorize(lambda a: bin(a).count("1") & 1)(i[:, None] & i[None, :])
+        assert np.array_equal(h, 1 - 2 * par)
+        assert np.array_equal(h @ h.T, g * np.eye(g, dtype=np.int64))
+
+
+@pytest.mark.parametrize("seed", [SEED, 0, 12345, 2 ** 64 - 1])
+def test_rotation_orthogonal_exactly(seed):
+    for g in GS:
+        r = o.rotation_matrix(g, seed)
+        k = math.log2(math.sqrt(g))
+        assert np.array_equal(np.abs(r), np.full((g, g), 2.0 ** -k))
+        assert np.array_equal(r @ r.T, np.eye(g))
+        assert np.array_equal(r.T @ r, np.eye(g))
+
+
+def test_rotation_signs_after_transform():
+    # (v . R)[j] = d[j] (v . H)[j] / sqrt(g): column j of R carries sign d[j]
+    for g in GS:
+        d = o.rotation_signs(SEED, g)
+        r = o.rotation_matrix(g, SEED)
+        assert np.array_equal(np.sign(r[0, :]).astype(np.int64), d)
+        assert np.all(r[:, 0] * d[0] > 0)
+
+
+def test_sign_prefix_and_counts():
+    d256 = o.rotation_signs(SEED, 256)
+    for g in (4, 16, 64):
+        assert np.array_equal(o.rotation_signs(SEED, g), d256[:g])
+    # 32-bit words of the g = 256 mask (bit i set <=> d[i] = -1), LSB first
+    bits = sum(1 << i for i in range(256) if d256[i] < 0)
+    words = [(bits >> (32 * w)) & 0xFFFFFFFF for w in range(8)]
+    assert words[0] == 0x2F06E2B7 and words[1] == 0x2CFCF23A
+    assert int((d256 < 0).sum()) == 140
+
+
+# --------------------------------------------------------------------------
+# P2: the rotation identity (x B)(W B)^T = x W^T
+# --------------------------------------------------------------------------
+
+def test_rotation_identity_unquantized():
+    x = o.bf16_to_f64(synth.TINY.x())
+    w = o.bf16_to_f64(synth.TINY.w())
+    for g in GS:
+        b = o.block_rotation(256, g, SEED)
+        lhs = (x @ b) @ (w @ b).T
+        rhs = x @ w.T
+        assert np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Number-format helpers against library routines
+# --------------------------------------------------------------------------
+
+def test_round_exact_to_f32_matches_numpy():
+    rng = np.random.default_rng(7)
+    cases = []
+    for _ in range(4000):
+        nbits = int(rng.integers(1, 53))
+        n = int(rng.integers(1, 2 ** nbits))
+        if rng.random() < 0.3:                     # force exact ties at 24 bits
+            n = ((n >> 1) << 1) | 1
+            n <<= 1
+        e = int(rng.integers(-200, 60))
+        if n.bit_length() + e > 127:
+            continue
+        cases.append((n if rng.random() < 0.5 else -n, e))
+    for n, e in cases:
+        ref = np.float32(np.float64(math.ldexp(float(n), e)))   # n < 2^53: exact in f64
+        got = o.round_exact_to_f32(n, e)
+        assert got.view(np.uint32) == ref.view(np.uint32), (n, e)
+
+
+def test_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(3)
+    a = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormals
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0, -0.0],
+                 dtype=np.float32),                                   # exact ties
+    ])
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.f32_to_bf16(a), ref)
+
+
+# --------------------------------------------------------------------------
+# Rotation of rows: brute force with exact rationals
+# --------------------------------------------------------------------------
+
+def _nearest_f32(fr: Fraction) -> np.float32:
+    """Independent correct rounding: try the float32 neighbours of a first
+    guess, pick the nearest, ties to the even significand."""
+    c0 = np.float32(float(fr))
+    cands = {c0, np.nextafter(c0, np.float32(np.inf)), np.nextafter(c0, np.float32(-np.inf))}
+    best = sorted(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                        int(np.float32(c).view(np.uint32)) & 1))[0]
+    return np.float32(best)
+
+
+def _bruteforce_rotate(x_bits, g, seed):
+    x = o.bf16_to_f64(x_bits)
+    h = o.hadamard(g)
+    d = o.rotation_signs(seed, g)
+    out = np.empty(x.shape, dtype=np.float32)
+    for r in range(x.shape[0]):
+        for q in range(0, x.shape[1], g):
+            xs = [Fraction(float(t)) for t in x[r, q:q + g]]
+            for j in range(g):
+                s = sum((xs[i] if h[i, j] > 0 else -xs[i]) for i in range(g))
+                out[r, q + j] = _nearest_f32(s * int(d[j]) / Fraction(math.isqrt(g)))
+    return out
+
+
+def _wide_span_rows(rows, k, seed):
+    """bf16 rows mixing ordinary values with tiny ones (exponent spans far
+    beyond 53 bits) and exact cancellations."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, k)).astype(np.float32) * 3
+    mask = rng.random((rows, k)) < 0.15
+    tiny = (rng.standard_normal((rows, k)) * 2.0 ** rng.integers(-140, -20, (rows, k)))
+    v = np.where(mask, tiny.astype(np.float32), v)
+    v[0, : k // 2] = 1.0                                     # cancellations
+    v[1, :] = 0.0
+    v[1, 0] = 2.0 ** -130                                    # subnormal bf16
+    return synth.f32_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("g", [4, 16])
+def test_rotate_rows_bruteforce_small_g(g):
+    xb = _wide_span_rows(6, 64, 11 + g)
+    want = _bruteforce_rotate(xb, g, SEED)
+    got, nflag = o.rotate_rows(xb, g, SEED, return_flag_count=True)
+    assert nflag > 0                      # the exact integer route is exercised
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    got2 = o.rotate_rows(xb, g, SEED, force_exact=True)
+    assert np.array_equal(got2.view(np.uint32), want.view(np.uint32))
+
+
+def test_rotate_rows_bruteforce_g256_rows():
+    xb = np.concatenate([_wide_span_rows(2, 256, 5), synth.TINY.x()[:1]])
+    want = _bruteforce_rotate(xb, 256, SEED)
+    got = o.rotate_rows(xb, 256, SEED)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_fast_and_exact_routes_agree_on_ordinary_data():
+    xb = synth.ZIMAGE_ATTN.scaled(m=8, k=1024).x()
+    for g in GS:
+        a, nflag = o.rotate_rows(xb, g, SEED, return_flag_count=True)
+        b = o.rotate_rows(xb, g, SEED, force_exact=True)
+        assert nflag == 0
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_gelu_tail_workload_has_wide_span_groups():
+    # a GELU of an outlier-scaled Gaussian puts values near 1e-15 beside
+    # values near 100 in the same group: the exact route must run there
+    xb = synth.FLUX_MLP_DOWN.x(rows=64)
+    _, nflag = o.rotate_rows(xb, 256, SEED, return_flag_count=True)
+    assert nflag > 0
+
+
+# --------------------------------------------------------------------------
+# P3: known answers for rotate + quantize
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", GS)
+def test_impulse_and_ones_known_answers(g):
+    k = 512
+    imp = np.zeros((1, k), dtype=np.float32)
+    imp[0, ::g] = 1.0
+    ones = np.ones((1, k), dtype=np.float32)
+    d = o.rotation_signs(SEED, g)
+    sq = math.isqrt(g)
+    xr = o.rotate_rows(synth.f32_to_bf16_bits(imp), g, SEED)
+    assert np.array_equal(xr[0], np.tile(d / sq, k // g).astype(np.float32))
+    xq, sx = o.quantize_activations(synth.f32_to_bf16_bits(imp), g, SEED)
+    assert np.array_equal(xq[0], np.tile(127 * d, k // g).astype(np.int8))
+    assert sx[0] == np.float32(np.float32(1.0 / sq) / np.float32(127.0))
+    xq, sx = o.quantize_activations(synth.f32_to_bf16_bits(ones), g, SEED)
+    want = np.zeros(k, dtype=np.int8)
+    want[::g] = 127 * d[0]
+    assert np.array_equal(xq[0], want)
+    assert sx[0] == np.float32(np.float32(sq) / np.float32(127.0))
+    if g == 256:
+        assert float(sx[0]) == float.fromhex("0x1.020408p-3")
+
+
+# --------------------------------------------------------------------------
+# P4: quantizer invariants
+# --------------------------------------------------------------------------
+
+def test_quantizer_invariants():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((64, 300)).astype(np.float32)
+    v[1] = 0.0
+    v[2] *= np.float32(1e-30)
+    v[3] *= np.float32(2.0 ** -100)                       # below the 2^-64 guard
+    v[4] = (rng.standard_normal(300) * 1e-42).astype(np.float32)   # subnormal
+    v[5] *= np.float32(1e30)
+    amax = np.abs(v).max(axis=1).astype(np.float32)
+    q, s = o.quantize_with_amax(v, amax)
+    assert q.dtype == np.int8 and q.min() >= -127
+    for r in range(v.shape[0]):
+        if amax[r] == 0:
+            assert s[r] == 0 and not q[r].any()
+            continue
+        assert np.abs(q[r].astype(np.int64)).max() == 127
+        assert s[r] == np.float32(amax[r] / np.float32(127.0))
+        if s[r] > np.float32(2.0 ** -120):                   # s itself not subnormal
+            err = np.abs(v[r].astype(np.float64) - float(s[r]) * q[r].astype(np.float64))
+            assert err.max() <= float(s[r]) * (0.5 + 2.0 ** -15)
+
+
+def test_tiny_guard_matches_plain_formula_where_finite():
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal((8, 64)) * 2.0 ** -90).astype(np.float32)
+    amax = np.abs(v).max(axis=1).astype(np.float32)
+    assert (amax < np.float32(2.0 ** -64)).all()
+    q, _ = o.quantize_with_amax(v, amax)
+    inv = (np.float32(127.0) / amax).astype(np.float32)
+    assert np.isfinite(inv).all()
+    plain = np.clip(np.rint((v * inv[:, None]).astype(np.float32)), -127, 127).astype(np.int8)
+    assert np.array_equal(q, plain)
+
+
+# --------------------------------------------------------------------------
+# P5: int32 GEMM by brute force
+# --------------------------------------------------------------------------
+
+def test_gemm_int32_bruteforce():
+    rng = np.random.default_rng(1)
+    xq = rng.integers(-127, 128, (64, 256)).astype(np.int8)
+    wq = rng.integers(-127, 128, (256, 256)).astype(np.int8)
+    want = np.einsum("mk,nk->mn", xq.astype(np.int64), wq.astype(np.int64))
+    assert np.array_equal(o.gemm_int32(xq, wq).astype(np.int64), want)
+    # extreme magnitudes over a long K stay exact
+    xq = np.full((3, 8192), 127, dtype=np.int8)
+    wq = np.full((2, 8192), -127, dtype=np.int8)
+    assert (o.gemm_int32(xq, wq) == -127 * 127 * 8192).all()
+
+
+def test_epilogue_closed_form():
+    acc = np.array([[0, 1, -1, 2 ** 24 + 1, -(2 ** 27) - 3]], dtype=np.int32)
+    s_w = np.float32(0.001)
+    s_x = np.array([0.5], dtype=np.float32)
+    y = o.epilogue(acc, s_w, s_x)
+    t = (acc.astype(np.float32) * s_w).astype(np.float32) * np.float32(0.5)
+    assert np.array_equal(y, o.f32_to_bf16(t.astype(np.float32)))
+    # 2^24 + 1 is not a float32: it rounds to 2^24 before scaling
+    assert acc.astype(np.float32)[0, 3] == np.float32(2 ** 24)
+
+
+# --------------------------------------------------------------------------
+# P6: dequant + derotate
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", GS)
+def test_dequant_integers_independent(g):
+    rng = np.random.default_rng(g)
+    wq = rng.integers(-127, 128, (8, 512)).astype(np.int8)
+    d = o.rotation_signs(SEED, g)
+    dh = np.diag(d) @ o.hadamard(g)
+    dense = np.kron(np.eye(512 // g, dtype=np.int64), dh)     # blockdiag(D H)
+    assert np.array_equal(o.derotation_integers(wq, g, SEED), wq.astype(np.int64) @ dense)
+    assert np.abs(o.derotation_integers(wq, g, SEED)).max() <= 127 * g
+
+
+@pytest.mark.parametrize("g", GS)
+def test_dequant_inverts_rotation_on_impulses(g):
+    k = 256
+    w = np.zeros((2, k), dtype=np.float32)
+    w[0, 0] = 1.0
+    w[1, 3] = -1.0
+    wq, s_w = o.quantize_weights(synth.f32_to_bf16_bits(w), g, SEED)
+    d = o.rotation_signs(SEED, g)
+    assert np.array_equal(wq[0, :g], (127 * d).astype(np.int8))
+    w_hat = o.bf16_to_f64(o.dequant_derotate(wq, s_w, g, SEED))
+    assert np.array_equal(w_hat, w.astype(np.float64))
+    ref = o.dequant_reference_f64(wq, s_w, g, SEED)
+    assert np.abs(ref - w).max() < 1e-6
+
+
+# --------------------------------------------------------------------------
+# P7, P8: reconstruction error and derotation on/off
+# --------------------------------------------------------------------------
+
+def _cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+@pytest.mark.parametrize("layer,g", [(synth.TINY, 256),
+                                     (synth.ZIMAGE_ATTN.scaled(n=512), 256),
+                                     (synth.QKV_SWEEP.scaled(n=256), 64),
+                                     (synth.QKV_SWEEP.scaled(n=256), 16)])
+def test_reconstruction_error_and_cosines(layer, g):
+    wb = layer.w()
+    w = o.bf16_to_f64(wb)
+    wq, s_w = o.quantize_weights(wb, g, SEED)
+    rec = o.dequant_reference_f64(wq, s_w, g, SEED)
+    e = np.linalg.norm(rec - w) / np.linalg.norm(w)
+    # uniform quantization noise: rms error = step / sqrt(12) (Bennett)
+    pred = float(s_w) / (math.sqrt(12.0) * math.sqrt(np.mean(w * w)))
+    assert abs(e / pred - 1.0) < 0.05
+    assert e < 0.05
+    # derotated cosine follows 1 - e^2/2; skipping derotation decorrelates
+    assert abs(_cos(rec, w) - (1 - e * e / 2)) < 1e-6
+    b = o.block_rotation(w.shape[1], g, SEED)
+    no_derot = float(s_w) * wq.astype(np.float64)
+    pred_ctrl = float(np.sum((w.T @ w) * b) / np.sum(w * w))
+    assert abs(_cos(no_derot, w) - pred_ctrl) < 0.01
+    assert abs(_cos(no_derot, w)) < 0.3
+
+
+def test_pages_cosine_error_pairing():
+    vals = dict(ln.split() for ln in _golden_lines("pages_decode_quality.txt"))
+    e = float(vals["relative_error"])
+    assert round(1 - e * e / 2, 5) == float(vals["cosine_derotated"])
+    assert float(vals["cosine_without_derotation"]) < 0.1
+
+
+# --------------------------------------------------------------------------
+# P10: rotation spreads outliers before per-token quantization
+# --------------------------------------------------------------------------
+
+def test_rotation_reduces_per_token_error():
+    xb = synth.ZIMAGE_ATTN.scaled(m=64, k=1024).x()
+    x = o.bf16_to_f64(xb)
+    xq, sx = o.quantize_activations(xb, 256, SEED)
+    b = o.block_rotation(1024, 256, SEED)
+    back = (sx[:, None].astype(np.float64) * xq) @ b.T
+    e_rot = np.linalg.norm(back - x) / np.linalg.norm(x)
+    x32 = x.astype(np.float32)
+    q, s = o.quantize_with_amax(x32, np.abs(x32).max(axis=1))
+    e_plain = np.linalg.norm(s[:, None] * q.astype(np.float64) - x) / np.linalg.norm(x)
+    assert e_rot < e_plain / 3
+
+
+# --------------------------------------------------------------------------
+# The whole int8 linear on the tiny workload
+# --------------------------------------------------------------------------
+
+def test_linear_int8_tiny_tolerances():
+    layer = synth.TINY
+    xb, wb = layer.x(), layer.w()
+    wq, s_w = o.quantize_weights(wb, 256, SEED)
+    y, xq, sx, acc = o.linear_int8(xb, wq, s_w, 256, SEED)
+    yb = o.bf16_to_f64(y)
+    ref = o.linear_int8_reference_f64(acc, s_w, sx)
+    assert o.rel_frobenius(yb, ref) < 2.0 ** -8
+    true = o.bf16_to_f64(xb) @ o.bf16_to_f64(wb).T
+    assert o.rel_frobenius(yb, true) < 0.05
+    deq = o.dequant_linear_reference_f64(xb, wq, s_w, 256, SEED)
+    assert o.rel_frobenius(deq, true) < 0.05

@@ -29,5 +29,5 @@ def test_student_t_columns_heavy_tailed():
 
 
 def test_bf16_round_trip():
-    v = np.array([1.0, 1.00390625, -2.5, 0.0, 3.0e38], dtype=np.float32)
+    v = np.array([1.0, 1.0078125, -2.5, 0.0, 2.0 ** 127], dtype=np.float32)
     assert np.array_equal(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)), v)

@@ -1,0 +1,158 @@
+/*
+ * convrot.h -- C ABI of the MI355X (gfx950) int8_tensorwise "convrot" linear layer.
+ *
+ * The layer (as the pages describe it):
+ *   - weights are stored int8 after a rotation of their input axis in g-wide
+ *     groups, with one fp32 scale per tensor (convert_to_quant guide, "What is
+ *     INT8 ConvRot?" and "How INT8 ConvRot Quantization Works");
+ *   - the default path dequantizes and derotates the weight on every forward
+ *     as an [out, in/g, g] @ [g, g] block matmul, then runs a bf16 linear
+ *     (PR "share the int8_convrot scheme ... Krea-2 and Z-Image", "What it is
+ *     worth");
+ *   - int8_compute rotates the input, quantizes it to int8 per token and
+ *     multiplies int8 by int8, slicing the tokens so that its working memory
+ *     stays within the default path's (Invoke docs "int8 Compute",
+ *     introduction and "Memory").
+ *
+ * The rotation R is not printed on the pages. This library fixes
+ *   R = H_g . diag(d) / sqrt(g),  g in {4, 16, 64, 256},
+ * with H_g Sylvester's Hadamard matrix (H[i][j] = (-1)^popcount(i & j)) and
+ * d[i] = -1 where bit 63 of SplitMix64 output i (counter form:
+ * mix(rot_seed + (i + 1) * 0x9E3779B97F4A7C15)) is set, else +1. The same R
+ * serves every group of every layer and both paths. `g` and `rot_seed` must
+ * be the same at quantize time and at use time; a mismatch is not detectable
+ * here, and decoding with the wrong rotation raises no error but gives noise
+ * (PR "share the int8_convrot scheme ... Krea-2 and Z-Image", QA Instructions).
+ *
+ * Numerics (bit-exact contract):
+ *   x_r  = each rotated element is the exact sum rounded once to fp32
+ *          (nearest-even);
+ *   s    = RN(amax / 127), inv = RN(127 / amax) (amax and the values scaled by
+ *          2^64 first when amax < 2^-64), q = rint_even(RN(x_r * inv)), so
+ *          |q| <= 127; amax == 0 gives s = 0 and q = 0;
+ *   W_hat = bf16(RN(float(S) * RN(s_w * 2^-log2(sqrt g)))), S = (Wq . D) . H;
+ *   y    = bf16(RN(RN(float(acc) * s_w) * s_x[m]) [+ bias[n] in fp32]).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous memory whose
+ *     last axis is K (input features). bf16 tensors are passed as uint16_t*.
+ *     Scales (s_w, s_x) live in device memory too.
+ *   - The caller owns every buffer. The library allocates and frees nothing
+ *     and keeps no state between calls (apart from a per-thread error string).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; the library never synchronizes. The
+ *     return value covers argument checks and launch errors; a fault inside a
+ *     kernel surfaces at the caller's next synchronization.
+ *   - Arguments are checked before anything is launched. On any error nothing
+ *     is enqueued and no output is touched.
+ *   - Shapes: K % 64 == 0, K % g == 0, K <= 16384 for the rotating entry points;
+ *     N % 16 == 0 and K <= 133144 (int32 accumulator bound) for the GEMM;
+ *     all dimensions < 2^31. M == 0 is a no-op (the M-sized buffers may then
+ *     be null).
+ *   - Alignment: tensor base pointers 16-byte aligned, scales 4-byte aligned.
+ *   - Results are bit-identical from run to run and independent of slicing.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVROT_ABI_VERSION 1
+
+typedef enum convrot_status {
+  CONVROT_OK = 0,
+  CONVROT_E_INVALID_ARG = 1,       /* null pointer, negative or zero dim, overlapping in/out  */
+  CONVROT_E_UNSUPPORTED_GROUP = 2, /* g not in {4,16,64,256}, or K % g != 0                   */
+  CONVROT_E_UNSUPPORTED_SHAPE = 3, /* a shape limit above is not met                          */
+  CONVROT_E_MISALIGNED = 4,        /* a pointer is not aligned as required                    */
+  CONVROT_E_WORKSPACE = 5,         /* workspace too small for one token row                   */
+  CONVROT_E_HIP = 6                /* a HIP call failed; see convrot_last_error_string()      */
+} convrot_status;
+
+/* Rotate, absmax and quantize a weight to int8 with one scale per tensor.
+ *   w   [n, k] bf16 (in)     the unquantized weight (out features x in features)
+ *   wq  [n, k] int8 (out)    Wq = q(W . blockdiag(R)) under the numerics above
+ *   s_w [1]    fp32 (out)    s_w = RN(amax / 127) over the whole rotated tensor
+ * Offline step of the format (convert_to_quant guide, "How INT8 ConvRot
+ * Quantization Works": --int8 --scaling_mode tensor --convrot
+ * --convrot-group-size). s_w's slot is also used as scratch while the call
+ * runs, so no other work may read it meanwhile. */
+convrot_status convrot_quantize_weights(const uint16_t* w, int64_t n, int64_t k, int g,
+                                        uint64_t rot_seed, int8_t* wq, float* s_w,
+                                        void* stream);
+
+/* Dequantize and derotate an int8 weight to bf16 (the default path's per-forward
+ * decode: PR "share the int8_convrot scheme ... Krea-2 and Z-Image", "What it is
+ * worth": an [out, in/g, g] @ [g, g] block matmul after the scale).
+ *   wq    [n, k] int8 (in), s_w [1] fp32 (in)
+ *   w_out [n, k] bf16 (out)  W_hat = s_w . Wq . blockdiag(R)^T, rounded as above */
+convrot_status convrot_dequant_derotate(const int8_t* wq, const float* s_w, int64_t n, int64_t k,
+                                        int g, uint64_t rot_seed, uint16_t* w_out, void* stream);
+
+/* Rotate each token row of x by blockdiag(R), take its absmax and quantize it to
+ * int8 with one fp32 scale per row (Invoke docs "int8 Compute", introduction).
+ *   x   [m, k] bf16 (in)
+ *   xq  [m, k] int8 (out), s_x [m] fp32 (out) */
+convrot_status convrot_quantize_activations(const uint16_t* x, int64_t m, int64_t k, int g,
+                                            uint64_t rot_seed, int8_t* xq, float* s_x,
+                                            void* stream);
+
+/* Test hook: the same result as convrot_quantize_activations, computed for every
+ * row by the exact (banded) kernel that otherwise only finishes the rows whose
+ * exponent span the fast kernel cannot sum exactly in float64. */
+convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, int64_t k, int g,
+                                                  uint64_t rot_seed, int8_t* xq, float* s_x,
+                                                  void* stream);
+
+/* int8 GEMM with the scaling epilogue (the int8 x int8 multiply of int8_compute:
+ * Invoke docs "int8 Compute", introduction).
+ *   xq [m, k] int8, s_x [m] fp32, wq [n, k] int8, s_w [1] fp32 (in)
+ *   bias [n] bf16 (in, nullable)
+ *   y   [m, n] bf16 (out, nullable)   y = bf16(RN(RN(float(acc) s_w) s_x[m]) [+ bias])
+ *   acc [m, n] int32 (out, nullable)  acc = xq . wq^T, exact
+ * At least one of y and acc must be non-null. */
+convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                 const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                                 int64_t k, uint16_t* y, int32_t* acc, void* stream);
+
+/* The int8_compute forward: for each slice of token rows, rotate + quantize the
+ * slice into the workspace, then run the int8 GEMM with the scaling epilogue.
+ * Slices hold as many rows as the workspace fits (Invoke docs "int8 Compute",
+ * "Memory": slices of at most twice the output width keep the working memory
+ * within the default path's bf16 unpack).
+ *   x [m, k] bf16, wq [n, k] int8, s_w [1] fp32, bias [n] bf16 nullable (in)
+ *   y [m, n] bf16 (out)
+ *   workspace: device memory, 256-byte aligned, workspace_bytes long; holds
+ *     slice_rows * k bytes of int8 activations (rounded up to 256) followed by
+ *     slice_rows fp32 scales. The output does not depend on the slice size. */
+convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const float* s_w,
+                                   const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
+                                   uint64_t rot_seed, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
+size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);
+
+/* Default workspace: slices of min(m, 2n) rows (Invoke docs "int8 Compute",
+ * "Memory"). Returns 0 for invalid dimensions. */
+size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/* Host-only: the rotation signs d[0..g) for (g, rot_seed) as +1/-1 bytes into
+ * host memory `d` (g bytes). Touches no GPU. */
+convrot_status convrot_rotation_signs(uint64_t rot_seed, int g, int8_t* d);
+
+const char* convrot_status_string(convrot_status s);
+/* Details of the last error on the calling thread ("" if none). */
+const char* convrot_last_error_string(void);
+int convrot_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

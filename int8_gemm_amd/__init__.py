@@ -1,0 +1,264 @@
+"""MI355X (gfx950) int8_tensorwise "convrot" linear layer.
+
+A thin binding of libconvrot.so (the C ABI declared in include/convrot.h):
+each function checks its torch tensors (device, dtype, contiguity), passes raw
+device pointers and the current HIP stream, and raises ConvrotError on a
+non-OK status. Every step of the computation runs in the library's HIP
+kernels; there is no other code path. The names follow the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "ConvrotError", "ROT_SEED", "load_library", "library_path",
+    "convrot_quantize_weights", "convrot_dequant_derotate", "convrot_quantize_activations",
+    "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_linear_int8",
+    "convrot_linear_int8_workspace_size", "convrot_linear_int8_workspace_for_rows",
+    "convrot_rotation_signs", "convrot_abi_version", "convrot_status_string",
+    "EXPORTED_SYMBOLS",
+]
+
+ROT_SEED = 0xC0FFEE
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libconvrot.so")
+_lib = None
+_lock = threading.Lock()
+
+# every extern "C" symbol that include/convrot.h declares
+EXPORTED_SYMBOLS = (
+    "convrot_quantize_weights", "convrot_dequant_derotate", "convrot_quantize_activations",
+    "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_linear_int8",
+    "convrot_linear_int8_workspace_for_rows", "convrot_linear_int8_workspace_size",
+    "convrot_rotation_signs", "convrot_status_string", "convrot_last_error_string",
+    "convrot_abi_version",
+)
+
+_STATUS = {0: "CONVROT_OK", 1: "CONVROT_E_INVALID_ARG", 2: "CONVROT_E_UNSUPPORTED_GROUP",
+           3: "CONVROT_E_UNSUPPORTED_SHAPE", 4: "CONVROT_E_MISALIGNED", 5: "CONVROT_E_WORKSPACE",
+           6: "CONVROT_E_HIP"}
+
+
+class ConvrotError(RuntimeError):
+    """A non-OK status from libconvrot (argument check or HIP launch error)."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libconvrot.so (built in-tree by __graft_entry__.build() or
+    int8_gemm_amd/_build.py). Raises if it is missing: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libconvrot.so is not built ({_LIB_PATH}); run "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, U64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, \
+            ctypes.c_size_t
+        sig = {
+            "convrot_quantize_weights": [P, I64, I64, I, U64, P, P, P],
+            "convrot_dequant_derotate": [P, P, I64, I64, I, U64, P, P],
+            "convrot_quantize_activations": [P, I64, I64, I, U64, P, P, P],
+            "convrot_quantize_activations_exact": [P, I64, I64, I, U64, P, P, P],
+            "convrot_gemm_int8": [P, P, P, P, P, I64, I64, I64, P, P, P],
+            "convrot_linear_int8": [P, P, P, P, I64, I64, I64, I, U64, P, P, SZ, P],
+            "convrot_rotation_signs": [U64, I, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.convrot_linear_int8_workspace_for_rows.argtypes = [I64, I64]
+        lib.convrot_linear_int8_workspace_for_rows.restype = SZ
+        lib.convrot_linear_int8_workspace_size.argtypes = [I64, I64, I64]
+        lib.convrot_linear_int8_workspace_size.restype = SZ
+        lib.convrot_status_string.argtypes = [I]
+        lib.convrot_status_string.restype = ctypes.c_char_p
+        lib.convrot_last_error_string.argtypes = []
+        lib.convrot_last_error_string.restype = ctypes.c_char_p
+        lib.convrot_abi_version.argtypes = []
+        lib.convrot_abi_version.restype = I
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise ConvrotError(status, lib.convrot_last_error_string().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a ROCm device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {devs}")
+
+
+def convrot_abi_version() -> int:
+    return load_library().convrot_abi_version()
+
+
+def convrot_status_string(status: int) -> str:
+    return load_library().convrot_status_string(status).decode()
+
+
+def convrot_rotation_signs(rot_seed: int, g: int) -> list[int]:
+    """Host-only: the rotation signs d[0..g) as +1/-1 ints."""
+    buf = (ctypes.c_int8 * g)()
+    _check(load_library().convrot_rotation_signs(rot_seed, g, buf))
+    return list(buf)
+
+
+def convrot_quantize_weights(w: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                             wq: torch.Tensor | None = None, s_w: torch.Tensor | None = None):
+    """W bf16 [n, k] -> (Wq int8 [n, k], s_w fp32 [1])."""
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    wq = torch.empty((n, k), dtype=torch.int8, device=w.device) if wq is None else wq
+    s_w = torch.empty(1, dtype=torch.float32, device=w.device) if s_w is None else s_w
+    _need(wq, "wq", torch.int8, 2)
+    _need(s_w, "s_w", torch.float32)
+    _same_device(w, wq, s_w)
+    _check(load_library().convrot_quantize_weights(_ptr(w), n, k, g, rot_seed, _ptr(wq),
+                                                   _ptr(s_w), _stream(w)))
+    return wq, s_w
+
+
+def convrot_dequant_derotate(wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                             rot_seed: int = ROT_SEED, *, out: torch.Tensor | None = None):
+    """Wq int8 [n, k], s_w fp32 [1] -> W_hat bf16 [n, k]."""
+    _need(wq, "wq", torch.int8, 2)
+    _need(s_w, "s_w", torch.float32)
+    n, k = wq.shape
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=wq.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(wq, s_w, out)
+    _check(load_library().convrot_dequant_derotate(_ptr(wq), _ptr(s_w), n, k, g, rot_seed,
+                                                   _ptr(out), _stream(wq)))
+    return out
+
+
+def _quant_act(fn_name, x, g, rot_seed, xq, s_x):
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device) if xq is None else xq
+    s_x = torch.empty(m, dtype=torch.float32, device=x.device) if s_x is None else s_x
+    _need(xq, "xq", torch.int8, 2)
+    _need(s_x, "s_x", torch.float32, 1)
+    _same_device(x, xq, s_x)
+    _check(getattr(load_library(), fn_name)(_ptr(x), m, k, g, rot_seed, _ptr(xq), _ptr(s_x),
+                                            _stream(x)))
+    return xq, s_x
+
+
+def convrot_quantize_activations(x: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                                 xq: torch.Tensor | None = None,
+                                 s_x: torch.Tensor | None = None):
+    """x bf16 [m, k] -> (xq int8 [m, k], s_x fp32 [m]), per-token scales."""
+    return _quant_act("convrot_quantize_activations", x, g, rot_seed, xq, s_x)
+
+
+def convrot_quantize_activations_exact(x: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                                       xq: torch.Tensor | None = None,
+                                       s_x: torch.Tensor | None = None):
+    """Test hook: the same result through the exact (banded) kernel only."""
+    return _quant_act("convrot_quantize_activations_exact", x, g, rot_seed, xq, s_x)
+
+
+def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
+                      bias: torch.Tensor | None = None, *, want_y: bool = True,
+                      want_acc: bool = False, y: torch.Tensor | None = None,
+                      acc: torch.Tensor | None = None):
+    """int8 GEMM + epilogue. Returns (y bf16 [m, n] or None, acc int32 [m, n] or None)."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(wq, "wq", torch.int8, 2)
+    _need(s_x, "s_x", torch.float32, 1)
+    _need(s_w, "s_w", torch.float32)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    if y is not None:
+        _need(y, "y", torch.bfloat16, 2)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, 2)
+    _same_device(xq, s_x, wq, s_w, bias, y, acc)
+    _check(load_library().convrot_gemm_int8(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w),
+                                            _ptr(bias), m, n, k, _ptr(y), _ptr(acc),
+                                            _stream(xq)))
+    return y, acc
+
+
+def convrot_linear_int8_workspace_size(m: int, n: int, k: int) -> int:
+    return int(load_library().convrot_linear_int8_workspace_size(m, n, k))
+
+
+def convrot_linear_int8_workspace_for_rows(rows: int, k: int) -> int:
+    return int(load_library().convrot_linear_int8_workspace_for_rows(rows, k))
+
+
+def convrot_linear_int8(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                        rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The int8_compute forward: x bf16 [m, k] -> y bf16 [m, n]. `workspace`
+    (uint8 on the device) defaults to the library's default size."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(wq, "wq", torch.int8, 2)
+    _need(s_w, "s_w", torch.float32)
+    m, k = x.shape
+    n = wq.shape[0]
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_int8_workspace_size(m, n, k), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(x, wq, s_w, bias, workspace, out)
+    _check(load_library().convrot_linear_int8(_ptr(x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k,
+                                              g, rot_seed, _ptr(out), _ptr(workspace),
+                                              workspace.numel(), _stream(x)))
+    return out

@@ -1,0 +1,276 @@
+// C ABI of the convrot library: argument checks, rotation signs, slicing.
+// Every check runs before any HIP call, so argument errors are reported
+// (and testable) without a GPU.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/convrot.h"
+#include "common.h"
+#include "internal.h"
+
+using namespace convrot;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+convrot_status fail(convrot_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+convrot_status fail(convrot_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+convrot_status ok() {
+  g_last_error[0] = '\0';
+  return CONVROT_OK;
+}
+
+convrot_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CONVROT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// SplitMix64 (Steele, Lea, Flood, OOPSLA 2014), counter form:
+// output i = mix(seed + (i + 1) * golden gamma).
+uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+SignMask make_signs(uint64_t seed, int g) {
+  SignMask sm;
+  memset(&sm, 0, sizeof sm);
+  for (int i = 0; i < g; ++i) {
+    const uint64_t z = splitmix64_mix(seed + (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull);
+    if (z >> 63) sm.w[i >> 5] |= 1u << (i & 31);
+  }
+  return sm;
+}
+
+bool valid_group(int g) { return g == 4 || g == 16 || g == 64 || g == 256; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
+  return x0 < y1 && y0 < x1;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxRotK = 16384;
+constexpr int64_t kMaxGemmK = 133144;  // 127^2 * K < 2^31
+
+// Checks shared by the rotating entry points (rows x k with group g).
+convrot_status check_rot(const char* fn, int64_t rows, int64_t k, int g) {
+  if (rows < 0 || k <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: bad dims rows=%lld k=%lld", fn,
+                                      (long long)rows, (long long)k);
+  if (!valid_group(g)) return fail(CONVROT_E_UNSUPPORTED_GROUP, "%s: g=%d not in {4,16,64,256}",
+                                   fn, g);
+  if (k % g) return fail(CONVROT_E_UNSUPPORTED_GROUP, "%s: k=%lld not a multiple of g=%d", fn,
+                         (long long)k, g);
+  if (k % 64 || k > kMaxRotK || rows >= kMaxDim)
+    return fail(CONVROT_E_UNSUPPORTED_SHAPE,
+                "%s: need k %% 64 == 0, k <= %lld, rows < 2^31 (rows=%lld k=%lld)", fn,
+                (long long)kMaxRotK, (long long)rows, (long long)k);
+  return CONVROT_OK;
+}
+
+convrot_status check_gemm(const char* fn, int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n <= 0 || k <= 0)
+    return fail(CONVROT_E_INVALID_ARG, "%s: bad dims m=%lld n=%lld k=%lld", fn, (long long)m,
+                (long long)n, (long long)k);
+  if (k % 64 || n % 16 || k > kMaxGemmK || m >= kMaxDim || n >= kMaxDim)
+    return fail(CONVROT_E_UNSUPPORTED_SHAPE,
+                "%s: need k %% 64 == 0, n %% 16 == 0, k <= %lld (m=%lld n=%lld k=%lld)", fn,
+                (long long)kMaxGemmK, (long long)m, (long long)n, (long long)k);
+  return CONVROT_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int convrot_abi_version(void) { return CONVROT_ABI_VERSION; }
+
+const char* convrot_status_string(convrot_status s) {
+  switch (s) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_E_INVALID_ARG: return "invalid argument";
+    case CONVROT_E_UNSUPPORTED_GROUP: return "unsupported rotation group size";
+    case CONVROT_E_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case CONVROT_E_MISALIGNED: return "misaligned pointer";
+    case CONVROT_E_WORKSPACE: return "workspace too small";
+    case CONVROT_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* convrot_last_error_string(void) { return g_last_error; }
+
+convrot_status convrot_rotation_signs(uint64_t rot_seed, int g, int8_t* d) {
+  if (!d) return fail(CONVROT_E_INVALID_ARG, "convrot_rotation_signs: null output");
+  if (!valid_group(g))
+    return fail(CONVROT_E_UNSUPPORTED_GROUP, "convrot_rotation_signs: g=%d", g);
+  const SignMask sm = make_signs(rot_seed, g);
+  for (int i = 0; i < g; ++i) d[i] = ((sm.w[i >> 5] >> (i & 31)) & 1u) ? -1 : 1;
+  return ok();
+}
+
+convrot_status convrot_quantize_weights(const uint16_t* w, int64_t n, int64_t k, int g,
+                                        uint64_t rot_seed, int8_t* wq, float* s_w,
+                                        void* stream) {
+  const char* fn = "convrot_quantize_weights";
+  if (!w || !wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
+  if (convrot_status s = check_rot(fn, n, k, g)) return s;
+  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s_w, 4))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  if (overlap(w, (size_t)(n * k) * 2, wq, (size_t)(n * k)) ||
+      overlap(w, (size_t)(n * k) * 2, s_w, 4) || overlap(wq, (size_t)(n * k), s_w, 4))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  const SignMask sm = make_signs(rot_seed, g);
+  return hip_status(launch_quantize_tensor(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream),
+                    fn);
+}
+
+convrot_status convrot_dequant_derotate(const int8_t* wq, const float* s_w, int64_t n, int64_t k,
+                                        int g, uint64_t rot_seed, uint16_t* w_out,
+                                        void* stream) {
+  const char* fn = "convrot_dequant_derotate";
+  if (!wq || !s_w || !w_out) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
+  if (convrot_status s = check_rot(fn, n, k, g)) return s;
+  if (!aligned(wq, 16) || !aligned(w_out, 16) || !aligned(s_w, 4))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  if (overlap(wq, (size_t)(n * k), w_out, (size_t)(n * k) * 2) ||
+      overlap(s_w, 4, w_out, (size_t)(n * k) * 2))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  const SignMask sm = make_signs(rot_seed, g);
+  return hip_status(launch_dequant(wq, s_w, n, k, g, sm, w_out, (hipStream_t)stream), fn);
+}
+
+static convrot_status quantize_activations_impl(const char* fn, bool exact, const uint16_t* x,
+                                                int64_t m, int64_t k, int g, uint64_t rot_seed,
+                                                int8_t* xq, float* s_x, void* stream) {
+  if (convrot_status s = check_rot(fn, m, k, g)) return s;
+  if (m == 0) return ok();  // nothing to read or write; the M-sized buffers may be null
+  if (!x || !xq || !s_x) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(s_x, 4))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  if (overlap(x, (size_t)(m * k) * 2, xq, (size_t)(m * k)) ||
+      overlap(x, (size_t)(m * k) * 2, s_x, (size_t)m * 4) ||
+      overlap(xq, (size_t)(m * k), s_x, (size_t)m * 4))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  if (m == 0) return ok();
+  const SignMask sm = make_signs(rot_seed, g);
+  hipError_t e = exact ? launch_quantize_rows_exact(x, xq, s_x, m, (int)k, g, sm,
+                                                    (hipStream_t)stream)
+                       : launch_quantize_rows(x, xq, s_x, m, (int)k, g, sm, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+convrot_status convrot_quantize_activations(const uint16_t* x, int64_t m, int64_t k, int g,
+                                            uint64_t rot_seed, int8_t* xq, float* s_x,
+                                            void* stream) {
+  return quantize_activations_impl("convrot_quantize_activations", false, x, m, k, g, rot_seed,
+                                   xq, s_x, stream);
+}
+
+convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, int64_t k, int g,
+                                                  uint64_t rot_seed, int8_t* xq, float* s_x,
+                                                  void* stream) {
+  return quantize_activations_impl("convrot_quantize_activations_exact", true, x, m, k, g,
+                                   rot_seed, xq, s_x, stream);
+}
+
+convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                 const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                                 int64_t k, uint16_t* y, int32_t* acc, void* stream) {
+  const char* fn = "convrot_gemm_int8";
+  if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (convrot_status s = check_gemm(fn, m, n, k)) return s;
+  if (m == 0) return ok();  // the M-sized buffers may be null
+  if (!xq || !s_x || (!y && !acc)) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(s_x, 4) || !aligned(s_w, 4) ||
+      (bias && !aligned(bias, 8)) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  const size_t ny = (size_t)(m * n) * 2, na = (size_t)(m * n) * 4;
+  if (overlap(y, ny, xq, (size_t)(m * k)) || overlap(y, ny, wq, (size_t)(n * k)) ||
+      overlap(acc, na, xq, (size_t)(m * k)) || overlap(acc, na, wq, (size_t)(n * k)) ||
+      overlap(y, ny, acc, na))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  if (m == 0) return ok();
+  return hip_status(launch_gemm(xq, s_x, wq, s_w, bias, m, n, k, y, acc, (hipStream_t)stream),
+                    fn);
+}
+
+size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k) {
+  if (rows <= 0 || k <= 0) return 0;
+  return align_up((size_t)(rows * k), 256) + (size_t)rows * 4;
+}
+
+size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n <= 0 || k <= 0) return 0;
+  int64_t rows = m < 2 * n ? m : 2 * n;
+  if (rows < 1) rows = 1;
+  return convrot_linear_int8_workspace_for_rows(rows, k);
+}
+
+convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const float* s_w,
+                                   const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
+                                   uint64_t rot_seed, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* fn = "convrot_linear_int8";
+  if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (convrot_status s = check_rot(fn, m, k, g)) return s;
+  if (convrot_status s = check_gemm(fn, m, n, k)) return s;
+  if (m == 0) return ok();  // the M-sized buffers may be null
+  if (!x || !y || !workspace) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(s_w, 4) || !aligned(y, 16) ||
+      (bias && !aligned(bias, 8)) || !aligned(workspace, 256))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  // largest slice that fits: align256(r*k) + 4r <= bytes
+  int64_t rows_fit = (int64_t)(workspace_bytes / (size_t)(k + 4));
+  while (rows_fit > 0 && convrot_linear_int8_workspace_for_rows(rows_fit, k) > workspace_bytes)
+    --rows_fit;
+  if (rows_fit < 1)
+    return fail(CONVROT_E_WORKSPACE, "%s: %zu bytes hold no row (need %zu)", fn, workspace_bytes,
+                convrot_linear_int8_workspace_for_rows(1, k));
+  const size_t ny = (size_t)(m * n) * 2;
+  if (overlap(y, ny, x, (size_t)(m * k) * 2) || overlap(y, ny, wq, (size_t)(n * k)) ||
+      overlap(y, ny, workspace, workspace_bytes) ||
+      overlap(workspace, workspace_bytes, x, (size_t)(m * k) * 2) ||
+      overlap(workspace, workspace_bytes, wq, (size_t)(n * k)))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  if (m == 0) return ok();
+  // whole GEMM tiles per slice when the workspace allows
+  int64_t slice = rows_fit < m ? rows_fit : m;
+  if (slice < m && slice >= 256) slice -= slice % 256;
+  const SignMask sm = make_signs(rot_seed, g);
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       align_up((size_t)(slice * k), 256));
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t r0 = 0; r0 < m; r0 += slice) {
+    const int64_t rows = (m - r0) < slice ? (m - r0) : slice;
+    hipError_t e = launch_quantize_rows(x + r0 * k, xq, sx, rows, (int)k, g, sm, st);
+    if (e != hipSuccess) return hip_status(e, fn);
+    e = launch_gemm(xq, sx, wq, s_w, bias, rows, n, k, y + r0 * n, nullptr, st);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
+}  // extern "C"

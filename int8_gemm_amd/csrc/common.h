@@ -1,0 +1,46 @@
+// Shared device/host definitions of the convrot library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+// Sign vector d of the rotation (bit i set <=> d[i] = -1), i < g <= 256.
+// Passed by value as a kernel argument; the host derives it from the seed.
+struct SignMask {
+  uint32_t w[8];
+};
+
+__host__ __device__ constexpr int ilog2(int g) { return g <= 1 ? 0 : 1 + ilog2(g >> 1); }
+
+// Quiet NaN written to a per-row scale to mark a row that the exact
+// (banded) kernel must finish. It is never a valid scale.
+constexpr uint32_t kDeferredRow = 0x7FC0DEADu;
+
+// Bands of the exact rotation: each band spans at most kBand binades, so a
+// float64 Walsh-Hadamard transform over one band is exact (see rotate.hip).
+constexpr int kBand = 36;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 r = __builtin_convertvector((f2){lo, hi}, bf2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bool sign_bit(const SignMask& s, int i) {
+  return (s.w[i >> 5] >> (i & 31)) & 1u;
+}
+
+}  // namespace convrot

@@ -1,0 +1,27 @@
+// Internal launcher declarations of the convrot library.
+#pragma once
+
+#include "common.h"
+
+namespace convrot {
+
+// Rotate + quantize rows (per-row scales): fast kernel, then the exact kernel
+// over the rows it deferred.
+hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
+                                int g, const SignMask& sm, hipStream_t st);
+// Same result through the exact kernel only (used by tests of the fast path).
+hipError_t launch_quantize_rows_exact(const uint16_t* x, int8_t* xq, float* s, int64_t rows,
+                                      int K, int g, const SignMask& sm, hipStream_t st);
+// Rotate + quantize a tensor with one scale (the scale slot doubles as the
+// absmax accumulator until the last launch).
+hipError_t launch_quantize_tensor(const uint16_t* w, int8_t* wq, float* s_w, int64_t rows, int K,
+                                  int g, const SignMask& sm, hipStream_t st);
+// W_hat = bf16(float(S) * RN(s_w * 2^-log2(sqrt g))), S = (Wq . D) . H per group.
+hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t k, int g,
+                          const SignMask& sm, uint16_t* w_out, hipStream_t st);
+// acc = xq . wq^T (int32); y = bf16(RN(RN(float(acc) * s_w) * s_x[m]) [+ bias[n]]).
+hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
+                       const uint16_t* bias, int64_t m, int64_t n, int64_t k, uint16_t* y,
+                       int32_t* acc, hipStream_t st);
+
+}  // namespace convrot

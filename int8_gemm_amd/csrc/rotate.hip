@@ -1,0 +1,583 @@
+// Rotation + absmax + int8 quantization kernels (gfx950).
+//
+// Rotation: x_r[j] = sum_i x[i] R[i, j] over each g-group of a row, with
+// R = H_g . diag(d) / sqrt(g) (Sylvester H, d = +-1). The value kept is the
+// exact sum rounded once to fp32 (nearest-even). Every product bf16 * (+-2^-k)
+// is exact, so this is order independent; the kernels compute it with a
+// Walsh-Hadamard transform (butterflies) in float64:
+//
+//   * Fast kernel: if a group's nonzero elements span at most 45 - log2(g)
+//     binades, every butterfly partial sum is a multiple of the smallest
+//     element's quantum and below g times the largest element, so it fits
+//     53 bits and float64 is exact. Rows holding a group outside that bound
+//     (or rows too small for the folded scaling below) are left to the exact
+//     kernel: their scale slot receives the kDeferredRow NaN.
+//   * Exact kernel: splits each group's elements into bands of kBand
+//     binades (each band's transform is exact in float64), turns each band's
+//     sums into integers of the band's quantum and adds the bands bottom-up
+//     with exact floor division, carrying a sticky bit for the dropped
+//     fraction. The rounding is then exact whenever the top band's integer
+//     has at least 27 bits; otherwise the element is at least 2^16 times
+//     below the row's absmax and quantizes to 0 whatever its fp32 value.
+//
+// Quantization (per row or per tensor): s = RN(amax/127), inv = RN(127/amax)
+// (both operands scaled by 2^64 first when amax < 2^-64),
+// q = rint_even(RN(x_r * inv)); |q| <= 127 always; amax == 0 gives s = q = 0.
+//
+// Pages: the per-token rotate + quantize of int8_compute is the Invoke docs
+// "int8 Compute" introduction; the weight quantization (one scale per tensor,
+// rotation in groups of g) is the convert_to_quant guide, "How INT8 ConvRot
+// Quantization Works" and "Determining the Right ConvRot Group Size".
+
+#include "common.h"
+#include "internal.h"
+
+namespace convrot {
+
+namespace {
+
+constexpr float kQuantBias = 12583040.0f;   // 1.5 * 2^23 + 128: low byte = q + 128
+constexpr float kQuantPlain = 12582912.0f;  // 1.5 * 2^23: low byte = q (two's complement)
+
+// --- cross-lane helpers ------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const uint64_t b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(uint32_t)b, m);
+  const int hi = __shfl_xor((int)(uint32_t)(b >> 32), m);
+  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// In-lane radix-2 Walsh-Hadamard stages over the low log2(min(G, N)) index
+// bits of v[N]; stage h combines (j, j+h) into (a+b, a-b).
+template <int G, int N>
+__device__ __forceinline__ void fwht_inlane(double (&v)[N]) {
+  constexpr int L = G < N ? G : N;
+#pragma unroll
+  for (int h = 1; h < L; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const double a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// Spread the 4 bits of a nibble to bytes: bit i -> byte i = 0xFF.
+__device__ __forceinline__ uint32_t nibble_to_bytemask(uint32_t nib) {
+  return ((nib * 0x00204081u) & 0x01010101u) * 0xFFu;
+}
+
+// Exponent fields of a packed bf16 pair (sign cleared): the max, and the min
+// over nonzero elements taken as (field of bits-1), so zeros drop out (they
+// wrap to 0xFFFF) and a mantissa-zero power of two reads one binade low,
+// which only widens the measured span.
+__device__ __forceinline__ void span_acc(uint32_t w, us2& mx, us2& mn) {
+  const us2 m = __builtin_bit_cast(us2, w & 0x7FFF7FFFu);
+  mx = __builtin_elementwise_max(mx, m);
+  mn = __builtin_elementwise_min(mn, m - (us2)(1));
+}
+
+__device__ __forceinline__ uint32_t lane_pack(us2 v, bool is_max) {
+  const uint32_t a = v.x, b = v.y;
+  return is_max ? (a > b ? a : b) : (a < b ? a : b);
+}
+
+// span of a group in binades, from the reduced max bits and min (bits-1).
+// Returns -1 for an all-zero group.
+__device__ __forceinline__ int group_span(uint32_t mxbits, uint32_t mnbits) {
+  if (mnbits == 0xFFFFu) return -1;
+  const int emax = (int)(mxbits >> 7);
+  int emin = (int)((mnbits + 1u) >> 7);
+  if (mnbits >= 0x7F80u) emin = (int)(mnbits >> 7);  // cannot happen for finite input
+  emin = emin < 1 ? 1 : emin;
+  return emax - emin;
+}
+
+}  // namespace
+
+// ============================================================================
+// Fast kernel: 64 contiguous elements per lane; rows spread over a team of
+// T = K/64 lanes; rows_per_block rows per block.
+// ============================================================================
+
+template <int G>
+__global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
+    const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
+    int64_t rows, int K, int T, int rows_per_block, SignMask sm) {
+  constexpr int CH = 64;
+  constexpr int LOGG = ilog2(G);
+  constexpr int kMaxSpan = 45 - LOGG;
+  constexpr int NGL = G >= CH ? 1 : CH / G;  // groups held by one lane
+  __shared__ uint32_t s_rowmax[256];
+  __shared__ uint32_t s_rowflag[256];
+
+  const int tid = threadIdx.x;
+  const int r_in = tid / T;
+  const int c = tid - r_in * T;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block + r_in;
+  const bool active = (r_in < rows_per_block) && (row < rows);
+  if (tid < rows_per_block) {
+    s_rowmax[tid] = 0u;
+    s_rowflag[tid] = 0u;
+  }
+
+  // ---- load 64 bf16 (8 x 16 B) ----
+  uint32_t w[32];
+  if (active) {
+    const u4* p = reinterpret_cast<const u4*>(x + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u4 q = __builtin_nontemporal_load(p + i);
+      w[4 * i + 0] = q.x;
+      w[4 * i + 1] = q.y;
+      w[4 * i + 2] = q.z;
+      w[4 * i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = 0u;
+  }
+
+  // ---- exponent span per group ----
+  bool flagged = false;
+  {
+    constexpr int DW = (G >= CH ? CH : G) / 2;  // dwords per (lane part of a) group
+#pragma unroll
+    for (int gidx = 0; gidx < NGL; ++gidx) {
+      us2 mx = (us2)(0), mn = (us2)(0xFFFF);
+#pragma unroll
+      for (int i = 0; i < DW; ++i) span_acc(w[gidx * DW + i], mx, mn);
+      uint32_t a = lane_pack(mx, true), b = lane_pack(mn, false);
+      if constexpr (G == 256) {
+        uint32_t t = dpp_u32<kQuadXor1>(a); a = a > t ? a : t;
+        t = dpp_u32<kQuadXor2>(a); a = a > t ? a : t;
+        t = dpp_u32<kQuadXor1>(b); b = b < t ? b : t;
+        t = dpp_u32<kQuadXor2>(b); b = b < t ? b : t;
+      }
+      flagged |= group_span(a, b) > kMaxSpan;
+    }
+  }
+
+  // ---- widen, transform ----
+  double v[CH];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[2 * i] = (double)bf16lo(w[i]);
+    v[2 * i + 1] = (double)bf16hi(w[i]);
+  }
+  fwht_inlane<G, CH>(v);
+  if constexpr (G == 256) {
+    const int q = c & 3;  // position of this lane's 64-element part in its group
+    const double s1 = (q & 1) ? -1.0 : 1.0;
+    const double s2 = (q & 2) ? -1.0 : 1.0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s1, dpp_f64<kQuadXor1>(v[i]));
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s2, dpp_f64<kQuadXor2>(v[i]));
+  }
+
+  // u = RN32(y) (y = unscaled, unsigned sum); x_r = d_j * u * 2^-k for normal x_r
+  float u[CH];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    u[i] = (float)v[i];
+    amax = fmaxf(amax, fabsf(u[i]));
+  }
+
+  __syncthreads();
+  if (active) {
+    atomicMax(&s_rowmax[r_in], __float_as_uint(amax));
+    if (flagged) atomicOr(&s_rowflag[r_in], 1u);
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const float amax_u = __uint_as_float(s_rowmax[r_in]);
+  constexpr int KS = LOGG / 2;  // 1/sqrt(g) = 2^-KS
+  const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact when deferral is not needed
+  const bool deferred = s_rowflag[r_in] != 0u || !(amax_u <= 3.0e38f) ||
+                        (amax_u > 0.0f && amax_x < 0x1p-100f);
+  if (deferred) {
+    if (c == 0) scale[row] = __uint_as_float(kDeferredRow);
+    return;
+  }
+  float s, inv_u;
+  if (amax_u > 0.0f) {
+    s = amax_x / 127.0f;
+    const float inv = 127.0f / amax_x;
+    inv_u = inv * (1.0f / (float)(1 << KS));
+  } else {
+    s = 0.0f;
+    inv_u = 0.0f;
+  }
+  if (c == 0) scale[row] = s;
+
+  // sign bits of this lane's 64 outputs
+  uint32_t sg0, sg1;
+  if constexpr (G == 256) {
+    const int q = c & 3;
+    sg0 = sm.w[2 * q];
+    sg1 = sm.w[2 * q + 1];
+  } else if constexpr (G == 64) {
+    sg0 = sm.w[0];
+    sg1 = sm.w[1];
+  } else if constexpr (G == 16) {
+    sg0 = (sm.w[0] & 0xFFFFu) * 0x00010001u;
+    sg1 = sg0;
+  } else {
+    sg0 = (sm.w[0] & 0xFu) * 0x11111111u;
+    sg1 = sg0;
+  }
+
+  uint32_t outw[16];
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = u[4 * d + e] * inv_u;
+      b[e] = __float_as_uint(p + kQuantBias);  // q + 128 in the low byte
+    }
+    const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+    const uint32_t packed = t0 | t1;
+    const uint32_t nib = ((d < 8 ? sg0 : sg1) >> ((4 * d) & 31)) & 0xFu;
+    const uint32_t m = nibble_to_bytemask(nib);
+    // negate the bytes with d = -1 (biased: 256 - v never carries), unbias
+    outw[d] = ((packed ^ m) + (m & 0x01010101u)) ^ 0x80808080u;
+  }
+  u4* o = reinterpret_cast<u4*>(xq + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (u4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
+}
+
+// ============================================================================
+// Exact kernel: 32 contiguous elements per lane, team of T = K/32 lanes per
+// row. Modes: per-row quantize (optionally only rows carrying kDeferredRow),
+// per-tensor absmax (pass 1) and per-tensor quantize (pass 2).
+// ============================================================================
+
+enum ExactMode : int { kRowAll = 0, kRowDeferred = 1, kTensorMax = 2, kTensorQuant = 3 };
+
+template <int G>
+__global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
+    const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
+    uint32_t* __restrict__ tensor_amax, int64_t rows, int K, int T, int rows_per_block,
+    SignMask sm, int mode) {
+  constexpr int CH = 32;
+  constexpr int LOGG = ilog2(G);
+  constexpr int KS = LOGG / 2;
+  constexpr int NGL = G >= CH ? 1 : CH / G;  // groups held by one lane
+  constexpr int GE = G >= CH ? CH : G;       // elements of a group in one lane
+  constexpr int LPG = G >= CH ? G / CH : 1;  // lanes per group
+  __shared__ uint32_t s_rowmax[256];
+  __shared__ uint32_t s_rowflag[256];
+
+  const int tid = threadIdx.x;
+  const int r_in = tid / T;
+  const int c = tid - r_in * T;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block + r_in;
+  bool active = (r_in < rows_per_block) && (row < rows);
+  if (tid < rows_per_block) {
+    s_rowmax[tid] = 0u;
+    s_rowflag[tid] = 0u;
+  }
+  if (mode == kRowDeferred) {
+    // rows that the fast kernel finished are skipped as a whole
+    if (active) active = __float_as_uint(scale[row]) == kDeferredRow;
+    __syncthreads();
+    if (active && c == 0) s_rowflag[r_in] = 1u;
+    __syncthreads();
+    if (__syncthreads_or(active) == 0) return;
+  }
+
+  uint32_t w[16];
+  if (active) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 q = p[i];
+      w[4 * i + 0] = q.x;
+      w[4 * i + 1] = q.y;
+      w[4 * i + 2] = q.z;
+      w[4 * i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0u;
+  }
+
+  // per group: largest exponent field E and band count
+  int egrp[NGL];
+  int nb_lane = 0;
+#pragma unroll
+  for (int gidx = 0; gidx < NGL; ++gidx) {
+    us2 mx = (us2)(0), mn = (us2)(0xFFFF);
+#pragma unroll
+    for (int i = 0; i < GE / 2; ++i) span_acc(w[gidx * (GE / 2) + i], mx, mn);
+    uint32_t a = lane_pack(mx, true), b = lane_pack(mn, false);
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+      const uint32_t ta = (uint32_t)__shfl_xor((int)a, m);
+      const uint32_t tb = (uint32_t)__shfl_xor((int)b, m);
+      a = a > ta ? a : ta;
+      b = b < tb ? b : tb;
+    }
+    const int span = group_span(a, b);
+    int e = (int)(a >> 7);
+    egrp[gidx] = e < 1 ? 1 : e;
+    const int nb = span < 0 ? 0 : span / kBand + 1;
+    nb_lane = nb_lane > nb ? nb_lane : nb;
+  }
+  // all lanes run the same number of bands (empty bands add nothing)
+  int nb_all = nb_lane;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int t = __shfl_xor(nb_all, m);
+    nb_all = nb_all > t ? nb_all : t;
+  }
+
+  double V[CH];
+  uint32_t sticky = 0u;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) V[i] = 0.0;
+
+  for (int band = nb_all - 1; band >= 0; --band) {
+    // keep the widened inputs out of registers across bands: recompute them
+    // from the packed bf16 words each band (an empty asm marks the words as
+    // changed, so the conversions are not hoisted out of the loop)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(w[i]));
+    double F[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      const int f = (int)((bits >> 7) & 0xFFu);
+      const int fe = f < 1 ? 1 : f;
+      const int eg = egrp[i / GE];
+      const bool in_band = ((bits & 0x7FFFu) != 0u) && ((eg - fe) / kBand == band);
+      const float xv = __uint_as_float(bits << 16);
+      F[i] = in_band ? (double)xv : 0.0;
+    }
+    fwht_inlane<G, CH>(F);
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+      const double sg = ((c & m) != 0) ? -1.0 : 1.0;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) F[i] = __builtin_fma(F[i], sg, shfl_xor_f64(F[i], m));
+    }
+    // integers of the band quantum 2^q_b, q_b = E - (band+1)*kBand - 133
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int eg = egrp[i / GE];
+      const double I = __builtin_ldexp(F[i], (band + 1) * kBand + 133 - eg);
+      const double fl = __builtin_floor(V[i] * 0x1p-36);
+      sticky |= (V[i] != fl * 0x1p36) ? (1u << i) : 0u;
+      V[i] = I + fl;
+    }
+  }
+
+  // x_r = d_j * (2V + sticky) * 2^(q_0 - 1 - KS), rounded once to fp32
+  float xr[CH];
+  float amax = 0.0f;
+  const int base_j = (G >= CH) ? CH * (c % LPG) : 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int eg = egrp[i / GE];
+    const double W = 2.0 * V[i] + (double)((sticky >> i) & 1u);
+    const int j = (G >= CH) ? base_j + i : (i % G);
+    const double sgn = sign_bit(sm, j) ? -1.0 : 1.0;
+    xr[i] = (float)(sgn * __builtin_ldexp(W, eg - kBand - 133 - 1 - KS));
+    amax = fmaxf(amax, fabsf(xr[i]));
+  }
+
+  if (mode == kTensorMax) {
+    // wave max, then one atomic per wave
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    if ((tid & 63) == 0 && amax > 0.0f) atomicMax(tensor_amax, __float_as_uint(amax));
+    return;
+  }
+
+  float rmax;
+  if (mode == kTensorQuant) {
+    rmax = __uint_as_float(*tensor_amax);
+  } else {
+    __syncthreads();
+    if (active) atomicMax(&s_rowmax[r_in], __float_as_uint(amax));
+    __syncthreads();
+    rmax = __uint_as_float(s_rowmax[r_in]);
+  }
+  if (!active) return;
+
+  float s = 0.0f, inv = 0.0f, pre = 1.0f;
+  if (rmax > 0.0f) {
+    s = rmax / 127.0f;
+    float a = rmax;
+    if (a < 0x1p-64f) {
+      a *= 0x1p64f;
+      pre = 0x1p64f;
+    }
+    inv = 127.0f / a;
+  }
+  if (mode != kTensorQuant && c == 0) scale[row] = s;
+
+  uint32_t outw[CH / 4];
+#pragma unroll
+  for (int d = 0; d < CH / 4; ++d) {
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = (xr[4 * d + e] * pre) * inv;
+      b[e] = __float_as_uint(p + kQuantPlain);
+    }
+    const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+    outw[d] = t0 | t1;
+  }
+  uint4* o = reinterpret_cast<uint4*>(xq + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+  for (int i = 0; i < CH / 16; ++i)
+    o[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
+}
+
+__global__ void tensor_scale_init_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
+
+__global__ void tensor_scale_final_kernel(float* s_w) {
+  const float amax = __uint_as_float(*reinterpret_cast<uint32_t*>(s_w));
+  *s_w = amax > 0.0f ? amax / 127.0f : 0.0f;
+}
+
+// ============================================================================
+// Launchers
+// ============================================================================
+
+namespace {
+
+struct TeamShape {
+  int T;      // lanes per row
+  int block;  // threads per block
+  int rpb;    // rows per block
+};
+
+// Choose a block of whole waves holding as many whole rows as fit, with the
+// least idle lanes (at most 512 threads, at most 256 rows).
+TeamShape team_shape(int T) {
+  TeamShape best{T, 0, 0};
+  double best_waste = 2.0;
+  for (int waves = 1; waves <= 8; ++waves) {
+    const int threads = 64 * waves;
+    int rpb = threads / T;
+    if (rpb < 1) continue;
+    if (rpb > 256) rpb = 256;
+    const double waste = 1.0 - (double)(rpb * T) / threads;
+    if (waste < best_waste - 1e-9) {
+      best_waste = waste;
+      best.block = threads;
+      best.rpb = rpb;
+    }
+  }
+  return best;
+}
+
+template <int G>
+hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
+                       const SignMask& sm, hipStream_t st) {
+  const TeamShape ts = team_shape(K / 64);
+  const int64_t blocks = (rows + ts.rpb - 1) / ts.rpb;
+  hipLaunchKernelGGL(rotate_quant_fast_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0, st,
+                     x, xq, s, rows, K, ts.T, ts.rpb, sm);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,
+                        int64_t rows, int K, const SignMask& sm, int mode, hipStream_t st) {
+  const TeamShape ts = team_shape(K / 32);
+  const int64_t blocks = (rows + ts.rpb - 1) / ts.rpb;
+  hipLaunchKernelGGL(rotate_quant_exact_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0,
+                     st, x, xq, s, tensor_amax, rows, K, ts.T, ts.rpb, sm, mode);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
+                                int g, const SignMask& sm, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipError_t e;
+  switch (g) {
+    case 4: e = launch_fast<4>(x, xq, s, rows, K, sm, st); break;
+    case 16: e = launch_fast<16>(x, xq, s, rows, K, sm, st); break;
+    case 64: e = launch_fast<64>(x, xq, s, rows, K, sm, st); break;
+    default: e = launch_fast<256>(x, xq, s, rows, K, sm, st); break;
+  }
+  if (e != hipSuccess) return e;
+  switch (g) {
+    case 4: return launch_exact<4>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);
+    case 16: return launch_exact<16>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);
+    case 64: return launch_exact<64>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);
+    default: return launch_exact<256>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);
+  }
+}
+
+hipError_t launch_quantize_rows_exact(const uint16_t* x, int8_t* xq, float* s, int64_t rows,
+                                      int K, int g, const SignMask& sm, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  switch (g) {
+    case 4: return launch_exact<4>(x, xq, s, nullptr, rows, K, sm, kRowAll, st);
+    case 16: return launch_exact<16>(x, xq, s, nullptr, rows, K, sm, kRowAll, st);
+    case 64: return launch_exact<64>(x, xq, s, nullptr, rows, K, sm, kRowAll, st);
+    default: return launch_exact<256>(x, xq, s, nullptr, rows, K, sm, kRowAll, st);
+  }
+}
+
+hipError_t launch_quantize_tensor(const uint16_t* w, int8_t* wq, float* s_w, int64_t rows, int K,
+                                  int g, const SignMask& sm, hipStream_t st) {
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(s_w);
+  hipLaunchKernelGGL(tensor_scale_init_kernel, dim3(1), dim3(1), 0, st, amax_bits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows == 0) {
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(tensor_scale_final_kernel, dim3(1), dim3(1), 0, st, s_w);
+      e = hipGetLastError();
+    }
+    return e;
+  }
+  for (int mode : {(int)kTensorMax, (int)kTensorQuant}) {
+    switch (g) {
+      case 4: e = launch_exact<4>(w, wq, nullptr, amax_bits, rows, K, sm, mode, st); break;
+      case 16: e = launch_exact<16>(w, wq, nullptr, amax_bits, rows, K, sm, mode, st); break;
+      case 64: e = launch_exact<64>(w, wq, nullptr, amax_bits, rows, K, sm, mode, st); break;
+      default: e = launch_exact<256>(w, wq, nullptr, amax_bits, rows, K, sm, mode, st); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(tensor_scale_final_kernel, dim3(1), dim3(1), 0, st, s_w);
+  return hipGetLastError();
+}
+
+}  // namespace convrot

@@ -1,0 +1,136 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/convrot.h declares, rejects bad arguments before touching HIP, and its
+host-side sign generator agrees with the oracle's independent one."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int8_gemm_amd as cr
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cr.library_path()):
+        from int8_gemm_amd import _build
+        _build.build()
+    return cr.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(cr.EXPORTED_SYMBOLS) == _declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cr.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(convrot_[a-z0-9_]+)\b", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert cr.convrot_abi_version() == 1
+    for s in range(7):
+        assert cr.convrot_status_string(s)
+
+
+@pytest.mark.parametrize("seed", [synth.ROT_SEED, 0, 1, 2 ** 64 - 1, 0x123456789ABCDEF])
+@pytest.mark.parametrize("g", [4, 16, 64, 256])
+def test_signs_match_oracle(lib, seed, g):
+    assert cr.convrot_rotation_signs(seed, g) == list(oracle.rotation_signs(seed, g))
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced on error paths
+FAKE_MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _status(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+@pytest.mark.parametrize("g,k,want", [(512, 256, 2), (0, 256, 2), (3, 192, 2), (256, 320, 2),
+                                      (4, 100, 3), (64, 32832, 3), (256, 0, 1)])
+def test_rotating_entry_points_reject_bad_group_and_shape(lib, g, k, want):
+    for fn in ("convrot_quantize_activations", "convrot_quantize_activations_exact"):
+        assert _status(lib, fn, FAKE, 8, k, g, 1, FAKE, ctypes.c_void_p(1 << 24), None) == want
+    assert _status(lib, "convrot_quantize_weights", FAKE, 8, k, g, 1, ctypes.c_void_p(1 << 24),
+                   ctypes.c_void_p(1 << 28), None) == want
+    assert _status(lib, "convrot_dequant_derotate", FAKE, ctypes.c_void_p(1 << 24), 8, k, g, 1,
+                   ctypes.c_void_p(1 << 28), None) == want
+    assert lib.convrot_last_error_string()
+
+
+def test_null_and_misaligned_and_overlap(lib):
+    assert _status(lib, "convrot_quantize_activations", None, 8, 256, 256, 1, FAKE, FAKE,
+                   None) == 1
+    assert _status(lib, "convrot_quantize_activations", FAKE_MIS, 8, 256, 256, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28), None) == 4
+    # xq overlapping x
+    assert _status(lib, "convrot_quantize_activations", FAKE, 8, 256, 256, 1,
+                   ctypes.c_void_p((1 << 20) + 256), ctypes.c_void_p(1 << 28), None) == 1
+    # gemm: no output at all
+    assert _status(lib, "convrot_gemm_int8", FAKE, FAKE, FAKE, FAKE, None, 8, 16, 64, None,
+                   None, None) == 1
+    # gemm: n % 16, k % 64
+    assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 8, 24, 64,
+                   ctypes.c_void_p(1 << 28), None, None) == 3
+    assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 8, 32, 96,
+                   ctypes.c_void_p(1 << 28), None, None) == 3
+    # gemm: K beyond the int32 accumulator bound
+    assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 8, 32, 133184,
+                   ctypes.c_void_p(1 << 36), None, None) == 3
+
+
+def test_linear_workspace_rules(lib):
+    k = 3840
+    assert cr.convrot_linear_int8_workspace_for_rows(1, k) == 3840 + 4
+    assert cr.convrot_linear_int8_workspace_for_rows(3, 320) == 1024 + 12
+    assert cr.convrot_linear_int8_workspace_size(4608, 3840, k) == \
+        cr.convrot_linear_int8_workspace_for_rows(4608, k)
+    assert cr.convrot_linear_int8_workspace_size(100000, 16, k) == \
+        cr.convrot_linear_int8_workspace_for_rows(32, k)
+    # too small for one row
+    st = _status(lib, "convrot_linear_int8", FAKE, ctypes.c_void_p(1 << 24),
+                 ctypes.c_void_p(1 << 26), None, 8, 16, k, 256, 1, ctypes.c_void_p(1 << 28),
+                 ctypes.c_void_p(1 << 32), 1000, None)
+    assert st == 5
+    # misaligned workspace
+    st = _status(lib, "convrot_linear_int8", FAKE, ctypes.c_void_p(1 << 24),
+                 ctypes.c_void_p(1 << 26), None, 8, 16, k, 256, 1, ctypes.c_void_p(1 << 28),
+                 ctypes.c_void_p((1 << 32) + 16), 1 << 20, None)
+    assert st == 4
+
+
+def test_m_zero_is_a_noop(lib):
+    # no HIP call happens for M == 0 (this container has no GPU)
+    assert _status(lib, "convrot_quantize_activations", FAKE, 0, 256, 256, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28), None) == 0
+    assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 0, 32, 64,
+                   ctypes.c_void_p(1 << 28), None, None) == 0
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cr.convrot_quantize_activations(x, 256)

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels through the C ABI against the CPU oracle, on the
+same seeded inputs. Integer and bf16 outputs whose definition is exact are
+compared bit for bit (Wq, s_w, xq, s_x, acc, W_hat, y of the int8 path);
+float outputs are also checked against float64 references to 1e-2 relative
+Frobenius error."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int8_gemm_amd as cr
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = synth.ROT_SEED
+GS = (4, 16, 64, 256)
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import os
+    if not os.path.exists(cr.library_path()):
+        from int8_gemm_amd import _build
+        _build.build()
+    cr.load_library()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _announce(msg):
+    print(msg, flush=True)
+
+
+# reduced shapes spanning several GEMM tiles and ragged tails, with each
+# workload's K and value recipe
+REDUCED = [
+    (synth.TINY, 256),
+    (synth.ZIMAGE_ATTN.scaled(m=300, n=272), 256),
+    (synth.FLUX_MLP_UP.scaled(m=257, n=528), 256),
+    (synth.FLUX_MLP_DOWN.scaled(m=96, n=256), 256),
+    (synth.WAN_FFN_UP.scaled(m=130, n=400), 256),
+    (synth.WAN_FFN_DOWN.scaled(m=70, n=272), 256),
+] + [(synth.QKV_SWEEP.scaled(m=260, n=288), g) for g in GS]
+IDS = [f"{l.name}-g{g}" for l, g in REDUCED]
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_quantize_weights_bitexact(layer, g):
+    _announce(f"quantize_weights {layer.name} g={g}")
+    wb = layer.w()
+    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_dequant_bitexact_and_tolerance(layer, g):
+    _announce(f"dequant {layer.name} g={g}")
+    wq_ref, s_ref = oracle.quantize_weights(layer.w(), g, SEED)
+    wq = torch.from_numpy(wq_ref).to(DEV)
+    s_w = torch.tensor([s_ref], dtype=torch.float32, device=DEV)
+    w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
+    got = host_bits(w_hat)
+    assert np.array_equal(got, oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+    ref = oracle.dequant_reference_f64(wq_ref, s_ref, g, SEED)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(got), ref) < 1e-2
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_quantize_activations_bitexact(layer, g):
+    _announce(f"quantize_activations {layer.name} g={g}")
+    xb = layer.x()
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
+    for fn in (cr.convrot_quantize_activations, cr.convrot_quantize_activations_exact):
+        xq, sx = fn(dev_bf16(xb), g, SEED)
+        assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref)), fn.__name__
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), fn.__name__
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_gemm_bitexact(layer, g, with_bias):
+    _announce(f"gemm {layer.name} g={g} bias={with_bias}")
+    xq_ref, sx_ref = oracle.quantize_activations(layer.x(), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights(layer.w(), g, SEED)
+    bias_b = None
+    if with_bias:
+        bias_b = synth.f32_to_bf16_bits(
+            np.random.default_rng(7).standard_normal(layer.n).astype(np.float32))
+    y, acc = cr.convrot_gemm_int8(torch.from_numpy(xq_ref).to(DEV),
+                                  torch.from_numpy(sx_ref).to(DEV),
+                                  torch.from_numpy(wq_ref).to(DEV),
+                                  torch.tensor([s_ref], dtype=torch.float32, device=DEV),
+                                  None if bias_b is None else dev_bf16(bias_b), want_acc=True)
+    acc_ref = oracle.gemm_int32(xq_ref, wq_ref)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    y_ref = oracle.epilogue(acc_ref, s_ref, sx_ref, bias_b)
+    assert np.array_equal(host_bits(y), y_ref)
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_linear_int8_bitexact_and_tolerances(layer, g):
+    _announce(f"linear_int8 {layer.name} g={g}")
+    xb, wb = layer.x(), layer.w()
+    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    y_ref, xq_ref, sx_ref, acc_ref = oracle.linear_int8(xb, wq_ref, s_ref, g, SEED)
+    x = dev_bf16(xb)
+    wq = torch.from_numpy(wq_ref).to(DEV)
+    s_w = torch.tensor([s_ref], dtype=torch.float32, device=DEV)
+    y = cr.convrot_linear_int8(x, wq, s_w, g, SEED)
+    got = host_bits(y)
+    assert np.array_equal(got, y_ref)
+    yf = oracle.bf16_to_f64(got)
+    assert oracle.rel_frobenius(yf, oracle.linear_int8_reference_f64(acc_ref, s_ref, sx_ref)) \
+        < 1e-2
+    # the default (dequant) path, consumed by a bf16 matmul
+    w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
+    y_deq = (x.float() @ w_hat.float().t()).to(torch.bfloat16)
+    ref_deq = oracle.dequant_linear_reference_f64(xb, wq_ref, s_ref, g, SEED)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
+
+
+def test_slicing_invariance_and_determinism():
+    layer, g = synth.ZIMAGE_ATTN.scaled(m=1030, n=256), 256
+    xb = layer.x()
+    wq_ref, s_ref = oracle.quantize_weights(layer.w(), g, SEED)
+    x = dev_bf16(xb)
+    wq = torch.from_numpy(wq_ref).to(DEV)
+    s_w = torch.tensor([s_ref], dtype=torch.float32, device=DEV)
+    outs = []
+    for rows in (1030, 515, 258, 256, 100, 1):
+        ws = torch.empty(cr.convrot_linear_int8_workspace_for_rows(rows, layer.k),
+                         dtype=torch.uint8, device=DEV)
+        outs.append(host_bits(cr.convrot_linear_int8(x, wq, s_w, g, SEED, workspace=ws)))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    for _ in range(10):
+        assert np.array_equal(host_bits(cr.convrot_linear_int8(x, wq, s_w, g, SEED)), outs[0])
+
+
+# --------------------------------------------------------------------------
+# Edge cases
+# --------------------------------------------------------------------------
+
+def _edge_rows(k):
+    rng = np.random.default_rng(11)
+    rows = []
+    rows.append(np.zeros(k))                                   # zero row
+    rows.append(np.full(k, -0.0))                              # negative zeros
+    imp = np.zeros(k); imp[0] = 1.0; rows.append(imp)          # impulse
+    rows.append(np.ones(k))                                    # constant: cancellations
+    rows.append(rng.standard_normal(k) * 2.0 ** -100)          # below the 2^-64 guard
+    rows.append(rng.standard_normal(k) * 1e-42)                # subnormal bf16 values
+    r = rng.standard_normal(k) * 3                             # wide exponent spans
+    m = rng.random(k) < 0.2
+    r[m] = rng.standard_normal(m.sum()) * 2.0 ** rng.integers(-130, -30, m.sum())
+    rows.append(r)
+    r = rng.standard_normal(k); r[::7] = 1e-38; rows.append(r)  # tiny normals beside O(1)
+    rows.append(rng.standard_normal(k) * 1e30)                 # large
+    rows.append(np.where(rng.random(k) < 0.5, 1.0, -1.0) * 2.0 ** rng.integers(-20, 20, k))
+    return synth.f32_to_bf16_bits(np.array(rows, dtype=np.float32))
+
+
+@pytest.mark.parametrize("g", GS)
+@pytest.mark.parametrize("k", [256, 3072])
+def test_edge_rows_activations(g, k):
+    _announce(f"edge rows g={g} k={k}")
+    xb = _edge_rows(k)
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
+    for fn in (cr.convrot_quantize_activations, cr.convrot_quantize_activations_exact):
+        xq, sx = fn(dev_bf16(xb), g, SEED)
+        assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref)), fn.__name__
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), fn.__name__
+
+
+@pytest.mark.parametrize("g", GS)
+def test_edge_weights(g):
+    _announce(f"edge weights g={g}")
+    for wb in (_edge_rows(256), np.zeros((16, 256), dtype=np.uint16),
+               synth.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((16, 256))
+                                      .astype(np.float32) * 2.0 ** -110)):
+        wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
+        wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+        assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
+        assert np.array_equal(wq.cpu().numpy(), wq_ref)
+        w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
+        assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (2, 32, 128), (255, 16, 192), (257, 272, 320),
+                                   (33, 1040, 64), (512, 512, 4096)])
+def test_gemm_shapes(m, n, k):
+    _announce(f"gemm shape {m}x{n}x{k}")
+    rng = np.random.default_rng(m * 7 + n)
+    xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    wq = rng.integers(-127, 128, (n, k)).astype(np.int8)
+    xq[0, :] = 127
+    wq[0, :] = -127
+    sx = (rng.random(m) * 1e-3).astype(np.float32)
+    sw = np.float32(3e-4)
+    y, acc = cr.convrot_gemm_int8(torch.from_numpy(xq).to(DEV), torch.from_numpy(sx).to(DEV),
+                                  torch.from_numpy(wq).to(DEV),
+                                  torch.tensor([sw], dtype=torch.float32, device=DEV),
+                                  want_acc=True)
+    acc_ref = oracle.gemm_int32(xq, wq)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert np.array_equal(host_bits(y), oracle.epilogue(acc_ref, sw, sx))
+
+
+def test_m_zero_and_errors_on_device():
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
+    xq, sx = cr.convrot_quantize_activations(x, 256)
+    assert xq.shape == (0, 256)
+    with pytest.raises(cr.ConvrotError) as e:
+        cr.convrot_quantize_activations(torch.zeros((4, 320), dtype=torch.bfloat16,
+                                                    device=DEV), 256)
+    assert e.value.status_name == "CONVROT_E_UNSUPPORTED_GROUP"
+
+
+def test_wrong_rotation_gives_noise():
+    # decoding with a different seed raises nothing and decorrelates the weight
+    layer, g = synth.ZIMAGE_ATTN.scaled(n=256), 256
+    wb = layer.w()
+    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
+    good = oracle.bf16_to_f64(host_bits(cr.convrot_dequant_derotate(wq, s_w, g, SEED)))
+    bad = oracle.bf16_to_f64(host_bits(cr.convrot_dequant_derotate(wq, s_w, g, SEED + 1)))
+    w = oracle.bf16_to_f64(wb)
+
+    def cos(a, b):
+        return float((a * b).sum() / math.sqrt((a * a).sum() * (b * b).sum()))
+    assert cos(good, w) > 0.9999
+    assert abs(cos(bad, w)) < 0.3

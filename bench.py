@@ -1,0 +1,244 @@
+"""Benchmark of the MI355X int8 convrot linear layer.
+
+One step = one int8_compute forward of the Z-Image-like attention projection
+(x bf16 [4608, 3840] -> y bf16 [4608, 3840], W int8 [3840, 3840], g = 256,
+seeded Hadamard-sign rotation): convrot_linear_int8, i.e. the fused
+rotate + absmax + quantize kernel(s) followed by the int8 MFMA GEMM.
+
+value = 2*M*N*K / (time per step), in TOPS (int8 ops).
+
+Also measured, each with HIP events on the stream its kernels run on:
+  gemm       - the int8 GEMM kernel alone: TOPS and fraction of the 5.0 POP/s
+               int8 dense MFMA peak (the "roofline" object);
+  act_quant  - activation rotate + quantize: algorithmic 3 B per element +
+               4 B per token, GB/s and fraction of 8 TB/s;
+  dequant    - weight dequant + derotate: 1 B read + 2 B written per element
+               (+ 4 B scale), GB/s and fraction of 8 TB/s.
+Inputs are rotated over enough buffers that the bytes touched between two uses
+of one buffer exceed twice the 256 MB MALL, so HBM, not cache, is measured.
+
+cpu_baseline: the CPU oracle (numpy/float64, as it stands) timed on the
+host's cores over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_zimage_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "int8_gemm_amd", "csrc", "gemm.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle sample (10-30 s)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def _source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(n_launch_units: float):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    if it was taken on the current GEMM source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != _source_hash(GEMM_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def _events_time(fn, reps, stream):
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(ms) / len(ms), ms[0], ms[len(ms) // 2]
+
+
+def _cpu_baseline(layer, g, seed, target_s):
+    """The oracle's int8 forward (rotate + quantize + int32 GEMM + epilogue)
+    over row chunks of the same workload until ~target_s seconds pass."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    import oracle
+    xb, wb = layer.x(), layer.w()
+    wq, s_w = oracle.quantize_weights(wb, g, seed)
+    chunk = 512
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        r0 = rows_done % layer.m
+        oracle.linear_int8(np.ascontiguousarray(xb[r0:r0 + chunk]), wq, s_w, g, seed)
+        rows_done += min(chunk, layer.m - r0)
+        el = time.perf_counter() - t0
+        if el >= target_s or el > 30.0:
+            break
+    tops = 2.0 * rows_done * layer.n * layer.k / el / 1e12
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} token rows (chunks of {chunk}) of the {layer.m}x{layer.n}x"
+                      f"{layer.k} layer through oracle.linear_int8 (numpy float64 BLAS), "
+                      f"{el:.1f} s"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the layer shards by tokens or output features without communication, see "
+              "DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_gemm_amd as cr
+    import synth
+
+    cr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer, g, seed = synth.ZIMAGE_ATTN, 256, synth.ROT_SEED
+    m, n, k = layer.m, layer.n, layer.k
+    print(f"[bench] workload {layer.name} g={g}: generating inputs", file=sys.stderr, flush=True)
+    xb, wb = layer.x(), layer.w()
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, w = to_dev(xb), to_dev(wb)
+    wq, s_w = cr.convrot_quantize_weights(w, g, seed)
+    stream = torch.cuda.current_stream(dev)
+
+    # rotating buffer sets (> 2 x MALL between reuses)
+    x_bytes = m * k * 2
+    nrot_x = max(2, math.ceil(2 * MALL_BYTES / x_bytes) + 1)
+    xs = [x0] + [x0.clone() for _ in range(nrot_x - 1)]
+    ws = torch.empty(cr.convrot_linear_int8_workspace_size(m, n, k), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        cr.convrot_linear_int8(xs[i % nrot_x], wq, s_w, g, seed, workspace=ws, out=y)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    ops = 2.0 * m * n * k
+    value = ops / (ms_step * 1e-3) / 1e12
+
+    # ---- per-kernel timings (HIP events on the launch stream) ----
+    reps = max(args.steps, 10)
+    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    sx = torch.empty(m, dtype=torch.float32, device=dev)
+    cr.convrot_quantize_activations(x0, g, seed, xq=xq, s_x=sx)
+    act_ms, act_min, _ = _events_time(
+        lambda i: cr.convrot_quantize_activations(xs[i % nrot_x], g, seed, xq=xq, s_x=sx),
+        reps, stream)
+    gemm_ms, gemm_min, gemm_med = _events_time(
+        lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=y), reps, stream)
+    wset = n * k * 3
+    nrot_w = max(2, math.ceil(2 * MALL_BYTES / wset) + 1)
+    wqs = [wq] + [wq.clone() for _ in range(nrot_w - 1)]
+    outs = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for _ in range(nrot_w)]
+    deq_ms, deq_min, _ = _events_time(
+        lambda i: cr.convrot_dequant_derotate(wqs[i % nrot_w], s_w, g, seed,
+                                              out=outs[i % nrot_w]), reps, stream)
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    act_bytes = 3.0 * m * k + 4.0 * m
+    deq_bytes = 3.0 * n * k + 4.0
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    act_gbs = act_bytes / (act_ms * 1e-3) / 1e9
+    deq_gbs = deq_bytes / (deq_ms * 1e-3) / 1e9
+    traffic = _traffic(1)
+
+    result = {
+        "metric": "int8 convrot linear TOPS (+% int8 MFMA peak); dequant/act-quant GB/s "
+                  "(+% HBM)",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{layer.name}: x bf16 [{m},{k}] (0.5% outlier channels x30), "
+                               f"W int8 [{n},{k}] (1% outlier columns x10), g={g}, "
+                               "R = Walsh-Hadamard x seeded signs",
+                   "m": m, "n": n, "k": k, "g": g, "rot_seed": seed,
+                   "x_buffers_rotated": nrot_x},
+        "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel",
+                     "achieved": round(gemm_tops, 3), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic,
+                     "avg_ms": round(gemm_ms, 5), "min_ms": round(gemm_min, 5)},
+        "act_quant": {"GB/s": round(act_gbs, 1), "frac_hbm": round(act_gbs / PEAK_HBM_GBS, 4),
+                      "avg_ms": round(act_ms, 5), "min_ms": round(act_min, 5),
+                      "bytes": act_bytes},
+        "dequant": {"GB/s": round(deq_gbs, 1), "frac_hbm": round(deq_gbs / PEAK_HBM_GBS, 4),
+                    "avg_ms": round(deq_ms, 5), "min_ms": round(deq_min, 5),
+                    "bytes": deq_bytes, "buffers_rotated": nrot_w},
+        "linear_tops_frac_peak": round(value / PEAK_INT8_TOPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = _cpu_baseline(layer, g, seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -179,6 +179,11 @@ def main():
         reps, stream)
     gemm_ms, gemm_min, gemm_med = _events_time(
         lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=y), reps, stream)
+    tiles = {}
+    for t in (128, 192, 256):
+        t_ms, _, _ = _events_time(
+            lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=y, tile=t), reps, stream)
+        tiles[str(t)] = round(2.0 * m * n * k / (t_ms * 1e-3) / 1e12, 1)
     wset = n * k * 3
     nrot_w = max(2, math.ceil(2 * MALL_BYTES / wset) + 1)
     wqs = [wq] + [wq.clone() for _ in range(nrot_w - 1)]
@@ -225,7 +230,8 @@ def main():
                      "achieved": round(gemm_tops, 3), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic,
-                     "avg_ms": round(gemm_ms, 5), "min_ms": round(gemm_min, 5)},
+                     "avg_ms": round(gemm_ms, 5), "min_ms": round(gemm_min, 5),
+                     "tops_by_forced_tile": tiles},
         "act_quant": {"GB/s": round(act_gbs, 1), "frac_hbm": round(act_gbs / PEAK_HBM_GBS, 4),
                       "avg_ms": round(act_ms, 5), "min_ms": round(act_min, 5),
                       "bytes": act_bytes},

@@ -120,6 +120,13 @@ convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_
                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
                                  int64_t k, uint16_t* y, int32_t* acc, void* stream);
 
+/* Test / tuning hook: convrot_gemm_int8 with a forced block tile of tile x tile
+ * outputs (128, 192 or 256; 0 = the automatic choice). Same results. */
+convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                      const float* s_w, const uint16_t* bias, int64_t m,
+                                      int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
+                                      void* stream);
+
 /* The int8_compute forward: for each slice of token rows, rotate + quantize the
  * slice into the workspace, then run the int8 GEMM with the scaling epilogue.
  * Slices hold as many rows as the workspace fits (Invoke docs "int8 Compute",

@@ -33,9 +33,9 @@ _lock = threading.Lock()
 # every extern "C" symbol that include/convrot.h declares
 EXPORTED_SYMBOLS = (
     "convrot_quantize_weights", "convrot_dequant_derotate", "convrot_quantize_activations",
-    "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_linear_int8",
-    "convrot_linear_int8_workspace_for_rows", "convrot_linear_int8_workspace_size",
-    "convrot_rotation_signs", "convrot_status_string", "convrot_last_error_string",
+    "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_gemm_int8_tile",
+    "convrot_linear_int8", "convrot_linear_int8_workspace_for_rows",
+    "convrot_linear_int8_workspace_size", "convrot_rotation_signs", "convrot_status_string", "convrot_last_error_string",
     "convrot_abi_version",
 )
 
@@ -76,6 +76,7 @@ def load_library():
             "convrot_quantize_activations": [P, I64, I64, I, U64, P, P, P],
             "convrot_quantize_activations_exact": [P, I64, I64, I, U64, P, P, P],
             "convrot_gemm_int8": [P, P, P, P, P, I64, I64, I64, P, P, P],
+            "convrot_gemm_int8_tile": [P, P, P, P, P, I64, I64, I64, P, P, I, P],
             "convrot_linear_int8": [P, P, P, P, I64, I64, I64, I, U64, P, P, SZ, P],
             "convrot_rotation_signs": [U64, I, P],
         }
@@ -204,8 +205,9 @@ def convrot_quantize_activations_exact(x: torch.Tensor, g: int, rot_seed: int = 
 def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
                       bias: torch.Tensor | None = None, *, want_y: bool = True,
                       want_acc: bool = False, y: torch.Tensor | None = None,
-                      acc: torch.Tensor | None = None):
-    """int8 GEMM + epilogue. Returns (y bf16 [m, n] or None, acc int32 [m, n] or None)."""
+                      acc: torch.Tensor | None = None, tile: int = 0):
+    """int8 GEMM + epilogue. Returns (y bf16 [m, n] or None, acc int32 [m, n] or None).
+    `tile` != 0 forces the block tile (test / tuning hook convrot_gemm_int8_tile)."""
     _need(xq, "xq", torch.int8, 2)
     _need(wq, "wq", torch.int8, 2)
     _need(s_x, "s_x", torch.float32, 1)
@@ -225,9 +227,14 @@ def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w
     if acc is not None:
         _need(acc, "acc", torch.int32, 2)
     _same_device(xq, s_x, wq, s_w, bias, y, acc)
-    _check(load_library().convrot_gemm_int8(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w),
-                                            _ptr(bias), m, n, k, _ptr(y), _ptr(acc),
-                                            _stream(xq)))
+    lib = load_library()
+    if tile:
+        st = lib.convrot_gemm_int8_tile(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(bias), m,
+                                        n, k, _ptr(y), _ptr(acc), tile, _stream(xq))
+    else:
+        st = lib.convrot_gemm_int8(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k,
+                                   _ptr(y), _ptr(acc), _stream(xq))
+    _check(st)
     return y, acc
 
 

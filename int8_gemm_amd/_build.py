@@ -31,9 +31,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the convrot library)")
 
 
+# the GEMM keeps its MFMA accumulators in VGPRs (its waves are sized so that
+# they fit); otherwise the allocator shuffles accumulator blocks between
+# AGPR ranges every K-step
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

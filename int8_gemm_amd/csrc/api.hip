@@ -195,10 +195,12 @@ convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, 
                                    rot_seed, xq, s_x, stream);
 }
 
-convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
-                                 const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
-                                 int64_t k, uint16_t* y, int32_t* acc, void* stream) {
-  const char* fn = "convrot_gemm_int8";
+static convrot_status gemm_impl(const char* fn, const int8_t* xq, const float* s_x,
+                                const int8_t* wq, const float* s_w, const uint16_t* bias,
+                                int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc,
+                                int tile, void* stream) {
+  if (tile != 0 && tile != 128 && tile != 192 && tile != 256)
+    return fail(CONVROT_E_INVALID_ARG, "%s: tile=%d not supported", fn, tile);
   if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (convrot_status s = check_gemm(fn, m, n, k)) return s;
   if (m == 0) return ok();  // the M-sized buffers may be null
@@ -212,8 +214,22 @@ convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_
       overlap(y, ny, acc, na))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   if (m == 0) return ok();
-  return hip_status(launch_gemm(xq, s_x, wq, s_w, bias, m, n, k, y, acc, (hipStream_t)stream),
-                    fn);
+  return hip_status(
+      launch_gemm_tile(xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile, (hipStream_t)stream), fn);
+}
+
+convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                 const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                                 int64_t k, uint16_t* y, int32_t* acc, void* stream) {
+  return gemm_impl("convrot_gemm_int8", xq, s_x, wq, s_w, bias, m, n, k, y, acc, 0, stream);
+}
+
+convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                      const float* s_w, const uint16_t* bias, int64_t m,
+                                      int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
+                                      void* stream) {
+  return gemm_impl("convrot_gemm_int8_tile", xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile,
+                   stream);
 }
 
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k) {

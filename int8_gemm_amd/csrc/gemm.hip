@@ -7,15 +7,19 @@
 // "int8 Compute", introduction: the input is quantized per token and int8 is
 // multiplied by int8); the pages run it through Triton on NVIDIA, this is a
 // gfx950 design of its own:
-//   * block tile 256 x 256, 4 waves (2 x 2), wave tile 128 x 128;
-//   * v_mfma_i32_16x16x64_i8 with the weight rows in the A operand, so each
-//     lane's accumulators are 4 consecutive output columns of one row;
-//   * K-step 128 bytes, double-buffered in LDS (2 x 64 KB), global loads for
-//     the next step issued before the current step's MFMAs;
-//   * LDS rows of 128 B with the 16-byte chunk index XOR-swizzled by the row,
-//     so the 16-byte fragment reads of consecutive rows hit distinct banks;
-//   * tiles are walked in groups of rows, with the block index remapped so
-//     that the 8 XCDs each get a contiguous range of tiles (L2 reuse).
+//   * block tile BM x BN (templated: 256x256 with 8 waves in a 2 x 4 grid,
+//     192x192 and 128x128 with 4 waves in a 2 x 2 grid); v_mfma_i32_32x32x32_i8 (on gfx950 it sustains the full int8
+//     rate, while the 16x16x64 form sustains about half) with the weight rows
+//     in the A operand, so each lane's accumulators come in runs of 4
+//     consecutive output columns;
+//   * K-step BK = 64 bytes (a 128-byte step measured slower: fewer stages fit
+//     in LDS, so fewer bytes are in flight); an NS-deep ring of LDS stages filled by
+//     global_load_lds_dwordx4 (global -> LDS without VGPRs); one barrier per
+//     K-step; the loads for step s+NS-1 are issued right after that barrier;
+//   * LDS stage layout: row-major rows of BK bytes, weights then
+//     activations; each DMA instruction fills 1024 / BK rows (1 KB);
+//   * the block index is remapped so that each of the 8 XCDs gets a
+//     contiguous range of tiles, walked in groups of 8 tile rows (L2 reuse).
 // Both operands are K-contiguous ("TN"). K % 64 == 0, N % 16 == 0.
 
 #include "common.h"
@@ -25,35 +29,71 @@ namespace convrot {
 
 namespace {
 
-constexpr int BM = 256;         // rows of xq per block
-constexpr int BN = 256;         // rows of wq per block
-constexpr int BK = 128;         // K bytes per stage
-constexpr int NTHR = 256;
-constexpr int CHUNKS = BK / 16; // 16-byte chunks per tile row
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+// s_waitcnt on vmcnt only (expcnt, lgkmcnt left unconstrained); gfx9 encoding
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 0xF) | (0x7 << 4) | (0xF << 8) | ((V >> 4) << 14));
+}
 
-__global__ __launch_bounds__(NTHR, 1) void gemm_i8_kernel(
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4, SGPR base
+// + 32-bit VGPR offset): lane i writes LDS bytes [lds_base + 16 i, +16).
+// Written as inline asm so that the compiler's waitcnt model (which treats the
+// LDS write of the builtin form as pending LDS traffic and drains it around
+// every later LDS read) stays out of the way; completion is tracked by the
+// explicit vmcnt waits of the K-loop. The instruction has no VGPR result.
+__device__ __forceinline__ void dma16(const int8_t* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would force vmcnt(0) and drain the in-flight LDS-DMA stages. The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB>
+__global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_x, const int8_t* __restrict__ wq,
     const float* __restrict__ s_w, const uint16_t* __restrict__ bias, int M, int N, int K,
     int tiles_m, int tiles_n, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  // stage s: A(wq) tile at s*64K, B(xq) tile at s*64K + 32K
+  constexpr int NW = WM * WN;                   // waves: WM along m, WN along n
+  constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (m, n)
+  constexpr int NJ = WTM / 32, NI = WTN / 32;   // 32x32 MFMA tiles per wave (m, n)
+  constexpr int STAGE = (BM + BN) * BK;         // bytes per LDS stage
+  constexpr int RPI = 1024 / BK;                // rows per 1 KB DMA instruction
+  constexpr int CPR = BK / 16;                  // 16-byte chunks per row
+  constexpr int LW = (BM + BN) / (RPI * NW);    // DMA instructions per wave per stage
+  constexpr int H = BK / 32;                    // 32-k slices per K-step
+  static_assert(BK == 64 || BK == 128, "K-step");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * NW) == 0, "tile shape");
+  static_assert(NS >= 3, "the K-loop waits for stage s+1 before issuing stage s+NS-1");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wn = wave & 1;   // wave column block in N
-  const int wm = wave >> 1;  // wave row block in M
+  const int wn = wave % WN;
+  const int wm = wave / WN;
 
-  // ---- tile index: XCD-contiguous, grouped rows ----
+  // ---- tile index: XCD-contiguous ranges, grouped rows ----
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   {
-    const int nx = 8;
+    constexpr int nx = 8;
     const int per = (ntiles + nx - 1) / nx;
     const int xcd = bid % nx;
     const int loc = bid / nx;
-    const int full = ntiles - (per - 1) * nx;  // XCDs that get `per` tiles
+    const int full = ntiles - (per - 1) * nx;
     bid = (xcd < full) ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
   }
   constexpr int GROUP = 8;
@@ -62,126 +102,247 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_i8_kernel(
   const int first_m = grp * GROUP;
   const int gm = min(tiles_m - first_m, GROUP);
   const int in_grp = bid - grp * group_sz;
-  const int tile_m = first_m + in_grp % gm;
-  const int tile_n = in_grp / gm;
-  const int m0 = tile_m * BM;
-  const int n0 = tile_n * BN;
+  const int m0 = (first_m + in_grp % gm) * BM;
+  const int n0 = (in_grp / gm) * BN;
 
-  // ---- global -> register staging (8 chunks of each operand per thread) ----
-  uint4 ra[8], rb[8];
-  auto gload = [&](int k0) {
+  // ---- per-lane DMA sources: instruction t of this wave covers combined
+  // rows RPI*q .. RPI*q+RPI-1 (weights first, then activations); lane ->
+  // row RPI*q + lane/CPR, 16-byte chunk lane%CPR (whole L2 lines for BK=128) ----
+  // 32-bit byte offsets (host keeps M*K and N*K below 2^31); the region
+  // base pointer and the K-step offset go in SGPRs
+  uint32_t voff[LW];
+  bool is_w[LW];
+  int ldsoff[LW];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int id = u * NTHR + tid;
-      const int row = id >> 3;
-      const int c = id & 7;
-      const int k = k0 + 16 * c;
+  for (int t = 0; t < LW; ++t) {
+    const int q = wave * LW + t;
+    const int row = RPI * q + lane / CPR;
+    const int p = lane % CPR;
+    is_w[t] = (RPI * q) < BN;  // whole instruction in one region (BN % RPI == 0)
+    if (row < BN) {
       const int n = min(n0 + row, N - 1);
-      const int m = min(m0 + row, M - 1);
-      if (k < K) {
-        ra[u] = *reinterpret_cast<const uint4*>(wq + (int64_t)n * K + k);
-        rb[u] = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k);
+      voff[t] = (uint32_t)n * (uint32_t)K + 16u * p;
+    } else {
+      const int m = min(m0 + row - BN, M - 1);
+      voff[t] = (uint32_t)m * (uint32_t)K + 16u * p;
+    }
+    ldsoff[t] = q * 1024;
+  }
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  // wave-uniform operands of the DMA go through readfirstlane into SGPRs
+  auto uniform_ptr = [](const int8_t* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const int8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  };
+  auto issue = [&](int s, int slot) {
+#pragma unroll
+    for (int t = 0; t < LW; ++t) {
+      const int8_t* base = uniform_ptr((is_w[t] ? wq : xq) + (int64_t)s * BK);
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(lds_u32 + (uint32_t)(slot * STAGE + ldsoff[t]));
+      dma16(base, voff[t], dst);
+    }
+  };
+
+  v16i acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = (v16i){};
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  // 32x32x32 operands: lane -> row lane%32 of a 32-row block, 16-byte
+  // half lane/32 of the 32-byte k-slice h of the K-step
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  int aoff[NI], boff[NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) aoff[i] = (wn * WTN + i * 32 + fr) * BK + 16 * fh;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) boff[j] = BN * BK + (wm * WTM + j * 32 + fr) * BK + 16 * fh;
+
+  // Each K-step is H 32-k slices whose fragments alternate between two
+  // register sets X (even slices) and Y (odd slices): while the MFMAs of one
+  // slice run, the next slice's fragments are read. Before the last slice of
+  // step s, the barrier publishes stage s+1 (and frees the ring slot of stage
+  // s-1 for the next DMA), so the last slice's MFMAs overlap the reads of
+  // slice 0 of step s+1.
+  constexpr int NF = NI + NJ;
+  v4i xa[NI], xb[NJ], ya[NI], yb[NJ];
+  auto read_slice = [&](int s, int h, v4i (&fa)[NI], v4i (&fb)[NJ]) {
+    const uint8_t* base = lds + (s % NS) * STAGE + 32 * h;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[j] = *reinterpret_cast<const v4i*>(base + boff[j]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) fa[i] = *reinterpret_cast<const v4i*>(base + aoff[i]);
+  };
+  auto mfma_slice = [&](const v4i (&fa)[NI], const v4i (&fb)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // spread the NF reads of the next slice over the NI*NJ MFMAs of this one
+  auto sched_slice = [&]() {
+    constexpr int NM = NI * NJ;
+    constexpr int PER = NM / NF > 0 ? NM / NF : 1;
+    constexpr int NR = NM / PER < NF ? NM / PER : NF;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NF - NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+  };
+  auto wait_stage_runtime = [&](int p) {  // p = later stages allowed to stay pending
+    if (p >= NS - 2) {
+      wait_vmcnt<(NS - 2) * LW>();
+    } else if (p == 3) {
+      wait_vmcnt<3 * LW>();
+    } else if (p == 2) {
+      wait_vmcnt<2 * LW>();
+    } else if (p == 1) {
+      wait_vmcnt<LW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+  // the first H-1 slices of step s (slice 0 is already in X)
+  auto early_slices = [&](int s) {
+#pragma unroll
+    for (int h = 0; h + 1 < H; ++h) {
+      if (h % 2 == 0) {
+        read_slice(s, h + 1, ya, yb);
+        mfma_slice(xa, xb);
       } else {
-        ra[u] = make_uint4(0, 0, 0, 0);
-        rb[u] = make_uint4(0, 0, 0, 0);
+        read_slice(s, h + 1, xa, xb);
+        mfma_slice(ya, yb);
       }
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* a = lds + stage * 65536;
-    uint8_t* b = a + 32768;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int id = u * NTHR + tid;
-      const int row = id >> 3;
-      const int c = id & 7;
-      const int off = row * BK + 16 * swz(row, c);
-      *reinterpret_cast<uint4*>(a + off) = ra[u];
-      *reinterpret_cast<uint4*>(b + off) = rb[u];
+      sched_slice();
     }
   };
 
-  v4i acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const int fr = lane & 15;  // fragment row within a 16-row block
-  const int fq = lane >> 4;  // k-slice (16 B) within a 64-byte sub-step
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < nk) gload((ks + 1) * BK);
-    const uint8_t* a = lds + cur * 65536;
-    const uint8_t* b = a + 32768;
-    const int subs = min(2, (K - ks * BK) / 64);
-    for (int sub = 0; sub < subs; ++sub) {
-      const int c = 4 * sub + fq;
-      v4i af[8], bf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = wn * 128 + i * 16 + fr;
-        af[i] = *reinterpret_cast<const v4i*>(a + row * BK + 16 * swz(row, c));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = wm * 128 + j * 16 + fr;
-        bf[j] = *reinterpret_cast<const v4i*>(b + row * BK + 16 * swz(row, c));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nk) {
-      __syncthreads();
-      lstore(cur ^ 1);
-      __syncthreads();
+  wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
+  lds_barrier();
+  read_slice(0, 0, xa, xb);
+  const int steady = nk - (NS - 1);  // steps that also refill the ring
+  int s = 0;
+  for (; s < steady; ++s) {
+    early_slices(s);
+    wait_vmcnt<(NS - 3) * LW>();  // stage s+1 landed (stage s+NS-2 may be pending)
+    lds_barrier();
+    issue(s + NS - 1, (s + NS - 1) % NS);
+    read_slice(s + 1, 0, xa, xb);
+    mfma_slice(ya, yb);  // H is even: the last slice sits in Y
+    sched_slice();
+  }
+  for (; s < nk; ++s) {
+    early_slices(s);
+    if (s + 1 < nk) {
+      wait_stage_runtime(nk - 2 - s);
+      lds_barrier();
+      read_slice(s + 1, 0, xa, xb);
+      mfma_slice(ya, yb);
+      sched_slice();
+    } else {
+      mfma_slice(ya, yb);
     }
   }
 
-  // ---- epilogue: lane holds n = 4*(lane/16) + e (e < 4), m = lane % 16 ----
+  // ---- epilogue: 32x32 output layout: lane holds m = lane % 32 of the
+  // tile and n = 8*a + 4*(lane/32) + e for register 4a + e ----
   const float sw = *s_w;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + wm * 128 + j * 16 + fr;
+  for (int j = 0; j < NJ; ++j) {
+    const int m = m0 + wm * WTM + j * 32 + fr;
     if (m >= M) continue;
     const float sx = s_x[m];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + 4 * fq;
-      if (n >= N) continue;
-      const v4i v = acc[i][j];
-      if (acc_out) {
-        *reinterpret_cast<int4*>(acc_out + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
-      }
-      float f[4];
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = (float)v[e] * sw;
-        f[e] = f[e] * sx;
-      }
-      if (bias) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-        f[0] = f[0] + bf16lo(bb.x);
-        f[1] = f[1] + bf16hi(bb.x);
-        f[2] = f[2] + bf16lo(bb.y);
-        f[3] = f[3] + bf16hi(bb.y);
-      }
-      if (y) {
-        uint2 o;
-        o.x = pack_bf16x2(f[0], f[1]);
-        o.y = pack_bf16x2(f[2], f[3]);
-        *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = o;
+      for (int a = 0; a < 4; ++a) {
+        const int n = n0 + wn * WTN + i * 32 + 8 * a + 4 * fh;
+        if (n >= N) continue;
+        const v16i& v = acc[i][j];
+        if (acc_out) {
+          *reinterpret_cast<v4i*>(acc_out + (int64_t)m * N + n) =
+              (v4i){v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]};
+        }
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = (float)v[4 * a + e] * sw;
+          f[e] = f[e] * sx;
+        }
+        if (bias) {
+          const u2 bb = *reinterpret_cast<const u2*>(bias + n);
+          f[0] = f[0] + bf16lo(bb.x);
+          f[1] = f[1] + bf16hi(bb.x);
+          f[2] = f[2] + bf16lo(bb.y);
+          f[3] = f[3] + bf16hi(bb.y);
+        }
+        if (y) {
+          const u2 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+          *reinterpret_cast<u2*>(y + (int64_t)m * N + n) = o;
+        }
       }
     }
   }
+}
+
+struct TileCfg {
+  int bm, bn, ns, per_cu;
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB>
+hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
+                      const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
+                      hipStream_t st) {
+  constexpr int lds_bytes = NS * (BM + BN) * BK;
+  static_assert(lds_bytes <= 160 * 1024, "LDS");
+  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB>;
+  static bool attr = false;  // benign race: the call is idempotent
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int tiles_m = (m + BM - 1) / BM;
+  const int tiles_n = (n + BN - 1) / BN;
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(64 * WM * WN), lds_bytes, st, xq, s_x, wq, s_w,
+                     bias, m, n, k, tiles_m, tiles_n, y, acc);
+  return hipGetLastError();
+}
+
+// Pick the tile whose estimated time is least: rounds of concurrent tiles
+// over 256 CUs times the work of one tile, with a small penalty for the
+// lower operand reuse of smaller tiles.
+TileCfg choose_tile(int64_t m, int64_t n) {
+  const TileCfg cands[] = {{256, 256, 4, 1}, {192, 192, 6, 1}, {128, 128, 4, 2}};
+  const double eff[] = {1.0, 0.95, 0.8};
+  TileCfg best = cands[0];
+  double best_t = 1e300;
+  for (int c = 0; c < 3; ++c) {
+    const TileCfg& t = cands[c];
+    const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
+    const int64_t slots = 256LL * t.per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double time = (double)rounds * t.bm * t.bn * t.per_cu / eff[c];
+    if (time < best_t * 0.999) {
+      best_t = time;
+      best = t;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -190,18 +351,28 @@ hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, con
                        const uint16_t* bias, int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int32_t* acc, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  const int tiles_m = (int)((m + BM - 1) / BM);
-  const int tiles_n = (int)((n + BN - 1) / BN);
-  const int ntiles = tiles_m * tiles_n;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_i8_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
-    attr_set = true;
+  const TileCfg t = choose_tile(m, n);
+  if (t.bm == 256)
+    return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+  if (t.bm == 192)
+    return launch_cfg<192, 192, 64, 2, 2, 6, 1>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+  return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+}
+
+hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
+                            const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                            int64_t k, uint16_t* y, int32_t* acc, int tile, hipStream_t st) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (tile == 0) return launch_gemm(xq, s_x, wq, s_w, bias, m, n, k, y, acc, st);
+  const int M = (int)m, N = (int)n, Kk = (int)k;
+  switch (tile) {
+    case 256:
+      return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
+    case 192:
+      return launch_cfg<192, 192, 64, 2, 2, 6, 1>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
+    default:
+      return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
   }
-  hipLaunchKernelGGL(gemm_i8_kernel, dim3(ntiles), dim3(NTHR), 131072, st, xq, s_x, wq, s_w, bias,
-                     (int)m, (int)n, (int)k, tiles_m, tiles_n, y, acc);
-  return hipGetLastError();
 }
 
 }  // namespace convrot

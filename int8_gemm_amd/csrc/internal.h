@@ -23,5 +23,9 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t
 hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                        const uint16_t* bias, int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int32_t* acc, hipStream_t st);
+// The same GEMM with a forced block tile (128, 192 or 256; 0 = automatic).
+hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
+                            const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                            int64_t k, uint16_t* y, int32_t* acc, int tile, hipStream_t st);
 
 }  // namespace convrot

@@ -203,10 +203,11 @@ def test_edge_weights(g):
         assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
 
 
+@pytest.mark.parametrize("tile", [0, 128, 192, 256])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (2, 32, 128), (255, 16, 192), (257, 272, 320),
-                                   (33, 1040, 64), (512, 512, 4096)])
-def test_gemm_shapes(m, n, k):
-    _announce(f"gemm shape {m}x{n}x{k}")
+                                   (33, 1040, 64), (512, 512, 4096), (400, 592, 384)])
+def test_gemm_shapes(m, n, k, tile):
+    _announce(f"gemm shape {m}x{n}x{k} tile={tile}")
     rng = np.random.default_rng(m * 7 + n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
     wq = rng.integers(-127, 128, (n, k)).astype(np.int8)
@@ -217,7 +218,7 @@ def test_gemm_shapes(m, n, k):
     y, acc = cr.convrot_gemm_int8(torch.from_numpy(xq).to(DEV), torch.from_numpy(sx).to(DEV),
                                   torch.from_numpy(wq).to(DEV),
                                   torch.tensor([sw], dtype=torch.float32, device=DEV),
-                                  want_acc=True)
+                                  want_acc=True, tile=tile)
     acc_ref = oracle.gemm_int32(xq, wq)
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert np.array_equal(host_bits(y), oracle.epilogue(acc_ref, sw, sx))

@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20
+SLEEP_CYCLES = 50_000_000  # GPU-side hold before a timed batch of launches
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_zimage_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "int8_gemm_amd", "csrc", "gemm.hip")
 
@@ -73,9 +74,15 @@ def _traffic(n_launch_units: float):
 
 
 def _events_time(fn, reps, stream):
+    """Per-launch GPU duration from HIP events recorded on `stream` around each
+    call. The stream is first held by a GPU sleep long enough for the host to
+    enqueue every call, so the events bracket the kernels alone, not host
+    launch gaps. Returns (mean, min, median) in ms."""
     import torch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SLEEP_CYCLES)
     for i in range(reps):
         starts[i].record(stream)
         fn(i)

@@ -24,6 +24,9 @@ __host__ __device__ constexpr int ilog2(int g) { return g <= 1 ? 0 : 1 + ilog2(g
 // (banded) kernel must finish. It is never a valid scale.
 constexpr uint32_t kDeferredRow = 0x7FC0DEADu;
 
+// Compute units of an MI355X (gfx950); sizes persistent grids.
+constexpr int kNumCUs = 256;
+
 // Bands of the exact rotation: each band spans at most kBand binades, so a
 // float64 Walsh-Hadamard transform over one band is exact (see rotate.hip).
 constexpr int kBand = 36;

@@ -91,22 +91,29 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
     fragN[0] = fragP[0];
   }
 
-  const float c = __builtin_nontemporal_load(s_w) * (1.0f / (float)(1 << KS));
-  const int64_t ntiles = (nrows + 31) / 32;
+  const float c = *s_w * (1.0f / (float)(1 << KS));
+  // work item = (32-row tile, JW consecutive output 32-blocks): the NB*NB
+  // MFMAs of a tile are spread over NB/JW waves (the tile's input bytes are
+  // re-read from L2 by each), which shortens each wave's serial MFMA chain.
+  constexpr int JW = NB < 2 ? NB : 2;
+  constexpr int NQ = NB / JW;
+  const int64_t nitems = (nrows + 31) / 32 * NQ;
   const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t wstride = (int64_t)gridDim.x * 4;
 
-  for (int64_t tile = wave0; tile < ntiles; tile += wstride) {
+  for (int64_t item = wave0; item < nitems; item += wstride) {
+    const int64_t tile = item / NQ;
+    const int jq = (int)(item % NQ);
     const int64_t r = tile * 32 + jl;                   // B column = this lane's view row
     const int64_t rr = r < nrows ? r : nrows - 1;
     v4i bfr[NB];
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
-      bfr[ib] = __builtin_nontemporal_load(
-          reinterpret_cast<const v4i*>(wq + rr * R + 32 * ib + 16 * kh));
+      bfr[ib] = *reinterpret_cast<const v4i*>(wq + rr * R + 32 * ib + 16 * kh);
     const bool ok = r < nrows;
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb) {
+    for (int jw = 0; jw < JW; ++jw) {
+      const int jb = jq * JW + jw;
       v16i acc = {};
 #pragma unroll
       for (int ib = 0; ib < NB; ++ib) {
@@ -114,17 +121,29 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
         acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(negb ? fragN[ib] : fragP[ib], bfr[ib], acc,
                                                      0, 0, 0);
       }
-      if (ok) {
-        uint16_t* o = out + r * R + 32 * jb + 4 * kh;
+      // lane (jl, kh) holds outputs j = 8a + 4kh + e of view row r; pack to
+      // bf16 pairs, then swap halves with lane jl + 32 (v_permlane32_swap) so
+      // that lane kh = 0 holds j = 16h .. 16h+7 and lane kh = 1 holds
+      // j = 16h+8 .. 16h+15 for h = 0, 1: two 16-byte stores per lane.
+      uint32_t pk[4][2];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float f0 = (float)acc[4 * a + 0] * c;
-          const float f1 = (float)acc[4 * a + 1] * c;
-          const float f2 = (float)acc[4 * a + 2] * c;
-          const float f3 = (float)acc[4 * a + 3] * c;
-          const u2 v = {pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
-          __builtin_nontemporal_store(v, reinterpret_cast<u2*>(o + 8 * a));
+      for (int a = 0; a < 4; ++a) {
+        pk[a][0] = pack_bf16x2((float)acc[4 * a + 0] * c, (float)acc[4 * a + 1] * c);
+        pk[a][1] = pack_bf16x2((float)acc[4 * a + 2] * c, (float)acc[4 * a + 3] * c);
+      }
+      uint16_t* o = out + r * R + 32 * jb + 8 * kh;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u4 v;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          // swap lanes 32..63 of pk[2h] with lanes 0..31 of pk[2h+1]
+          const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * h][e], pk[2 * h + 1][e],
+                                                           false, false);
+          v[e] = sw[0];      // kh = 0: own a = 2h; kh = 1: partner's a = 2h+1
+          v[2 + e] = sw[1];  // kh = 0: partner's a = 2h; kh = 1: own a = 2h+1
         }
+        if (ok) *reinterpret_cast<u4*>(o + 16 * h) = v;
       }
     }
   }
@@ -138,8 +157,8 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t
   if (ne == 0) return hipSuccess;
   const int R = g > 32 ? g : 32;
   const int64_t nrows = ne / R;
-  const int64_t tiles = (nrows + 31) / 32;
-  int64_t blocks = (tiles + 3) / 4;
+  const int64_t items = (nrows + 31) / 32 * (R >= 64 ? R / 64 : 1);
+  int64_t blocks = (items + 3) / 4;
   const int64_t cap = 256 * 8;
   if (blocks > cap) blocks = cap;
   switch (g) {

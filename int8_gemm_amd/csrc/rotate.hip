@@ -41,17 +41,18 @@ constexpr float kQuantPlain = 12582912.0f;  // 1.5 * 2^23: low byte = q (two's c
 
 // --- cross-lane helpers ------------------------------------------------------
 
+// quad permutations write every lane, so no "old" operand is needed
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
   return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
@@ -117,122 +118,39 @@ __device__ __forceinline__ int group_span(uint32_t mxbits, uint32_t mnbits) {
 }  // namespace
 
 // ============================================================================
-// Fast kernel: 64 contiguous elements per lane; rows spread over a team of
-// T = K/64 lanes; rows_per_block rows per block.
+// Fast kernel: 64 contiguous elements per lane; a row is spread over a team
+// of T = K/64 lanes; a block holds rows_per_block rows (one "batch") at a
+// time and walks batches blockIdx.x, blockIdx.x + gridDim.x, ... (persistent
+// grid). The next batch's bf16 words are loaded into registers while the
+// current batch is transformed. The per-row max and flag go through LDS
+// slots used round-robin over 3 batches, so one barrier per batch suffices:
+// the slot reset after batch b's barrier is that of batch b-1 (whose readers
+// all passed the barrier) and it is next written after batch b+1's barrier.
 // ============================================================================
 
 template <int G>
 __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
-    int64_t rows, int K, int T, int rows_per_block, SignMask sm) {
+    int64_t rows, int K, int T, int rows_per_block, int64_t nbatches, SignMask sm) {
   constexpr int CH = 64;
   constexpr int LOGG = ilog2(G);
   constexpr int kMaxSpan = 45 - LOGG;
   constexpr int NGL = G >= CH ? 1 : CH / G;  // groups held by one lane
-  __shared__ uint32_t s_rowmax[256];
-  __shared__ uint32_t s_rowflag[256];
+  constexpr int KS = LOGG / 2;               // 1/sqrt(g) = 2^-KS
+  __shared__ uint32_t s_rowmax[3][256];
+  __shared__ uint32_t s_rowflag[3][256];
 
   const int tid = threadIdx.x;
   const int r_in = tid / T;
   const int c = tid - r_in * T;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_block + r_in;
-  const bool active = (r_in < rows_per_block) && (row < rows);
+  const bool in_team = r_in < rows_per_block;
   if (tid < rows_per_block) {
-    s_rowmax[tid] = 0u;
-    s_rowflag[tid] = 0u;
-  }
-
-  // ---- load 64 bf16 (8 x 16 B) ----
-  uint32_t w[32];
-  if (active) {
-    const u4* p = reinterpret_cast<const u4*>(x + row * (int64_t)K + (int64_t)CH * c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u4 q = __builtin_nontemporal_load(p + i);
-      w[4 * i + 0] = q.x;
-      w[4 * i + 1] = q.y;
-      w[4 * i + 2] = q.z;
-      w[4 * i + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = 0u;
-  }
-
-  // ---- exponent span per group ----
-  bool flagged = false;
-  {
-    constexpr int DW = (G >= CH ? CH : G) / 2;  // dwords per (lane part of a) group
-#pragma unroll
-    for (int gidx = 0; gidx < NGL; ++gidx) {
-      us2 mx = (us2)(0), mn = (us2)(0xFFFF);
-#pragma unroll
-      for (int i = 0; i < DW; ++i) span_acc(w[gidx * DW + i], mx, mn);
-      uint32_t a = lane_pack(mx, true), b = lane_pack(mn, false);
-      if constexpr (G == 256) {
-        uint32_t t = dpp_u32<kQuadXor1>(a); a = a > t ? a : t;
-        t = dpp_u32<kQuadXor2>(a); a = a > t ? a : t;
-        t = dpp_u32<kQuadXor1>(b); b = b < t ? b : t;
-        t = dpp_u32<kQuadXor2>(b); b = b < t ? b : t;
-      }
-      flagged |= group_span(a, b) > kMaxSpan;
+    for (int q = 0; q < 3; ++q) {
+      s_rowmax[q][tid] = 0u;
+      s_rowflag[q][tid] = 0u;
     }
   }
-
-  // ---- widen, transform ----
-  double v[CH];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[2 * i] = (double)bf16lo(w[i]);
-    v[2 * i + 1] = (double)bf16hi(w[i]);
-  }
-  fwht_inlane<G, CH>(v);
-  if constexpr (G == 256) {
-    const int q = c & 3;  // position of this lane's 64-element part in its group
-    const double s1 = (q & 1) ? -1.0 : 1.0;
-    const double s2 = (q & 2) ? -1.0 : 1.0;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s1, dpp_f64<kQuadXor1>(v[i]));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s2, dpp_f64<kQuadXor2>(v[i]));
-  }
-
-  // u = RN32(y) (y = unscaled, unsigned sum); x_r = d_j * u * 2^-k for normal x_r
-  float u[CH];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    u[i] = (float)v[i];
-    amax = fmaxf(amax, fabsf(u[i]));
-  }
-
-  __syncthreads();
-  if (active) {
-    atomicMax(&s_rowmax[r_in], __float_as_uint(amax));
-    if (flagged) atomicOr(&s_rowflag[r_in], 1u);
-  }
-  __syncthreads();
-  if (!active) return;
-
-  const float amax_u = __uint_as_float(s_rowmax[r_in]);
-  constexpr int KS = LOGG / 2;  // 1/sqrt(g) = 2^-KS
-  const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact when deferral is not needed
-  const bool deferred = s_rowflag[r_in] != 0u || !(amax_u <= 3.0e38f) ||
-                        (amax_u > 0.0f && amax_x < 0x1p-100f);
-  if (deferred) {
-    if (c == 0) scale[row] = __uint_as_float(kDeferredRow);
-    return;
-  }
-  float s, inv_u;
-  if (amax_u > 0.0f) {
-    s = amax_x / 127.0f;
-    const float inv = 127.0f / amax_x;
-    inv_u = inv * (1.0f / (float)(1 << KS));
-  } else {
-    s = 0.0f;
-    inv_u = 0.0f;
-  }
-  if (c == 0) scale[row] = s;
 
   // sign bits of this lane's 64 outputs
   uint32_t sg0, sg1;
@@ -251,27 +169,139 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     sg1 = sg0;
   }
 
-  uint32_t outw[16];
+  auto load = [&](int64_t batch, uint32_t (&w)[32]) {
+    const int64_t row = batch * rows_per_block + r_in;
+    if (in_team && batch < nbatches && row < rows) {
+      const u4* p = reinterpret_cast<const u4*>(x + row * (int64_t)K + (int64_t)CH * c);
 #pragma unroll
-  for (int d = 0; d < 16; ++d) {
-    uint32_t b[4];
+      for (int i = 0; i < 8; ++i) {
+        const u4 q = p[i];
+        w[4 * i + 0] = q.x;
+        w[4 * i + 1] = q.y;
+        w[4 * i + 2] = q.z;
+        w[4 * i + 3] = q.w;
+      }
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = u[4 * d + e] * inv_u;
-      b[e] = __float_as_uint(p + kQuantBias);  // q + 128 in the low byte
+      for (int i = 0; i < 32; ++i) w[i] = 0u;
     }
-    const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
-    const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
-    const uint32_t packed = t0 | t1;
-    const uint32_t nib = ((d < 8 ? sg0 : sg1) >> ((4 * d) & 31)) & 0xFu;
-    const uint32_t m = nibble_to_bytemask(nib);
-    // negate the bytes with d = -1 (biased: 256 - v never carries), unbias
-    outw[d] = ((packed ^ m) + (m & 0x01010101u)) ^ 0x80808080u;
-  }
-  u4* o = reinterpret_cast<u4*>(xq + row * (int64_t)K + (int64_t)CH * c);
+  };
+
+  uint32_t w[32];
+  int64_t batch = blockIdx.x;
+  load(batch, w);
+  __syncthreads();  // slot initialisation visible
+
+  for (int it = 0; batch < nbatches; ++it, batch += gridDim.x) {
+    const int64_t row = batch * rows_per_block + r_in;
+    const bool active = in_team && row < rows;
+    uint32_t wn[32];
+    load(batch + gridDim.x, wn);
+
+    // ---- exponent span per group ----
+    bool flagged = false;
+    {
+      constexpr int DW = (G >= CH ? CH : G) / 2;  // dwords per (lane part of a) group
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = (u4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
+      for (int gidx = 0; gidx < NGL; ++gidx) {
+        us2 mx = (us2)(0), mn = (us2)(0xFFFF);
+#pragma unroll
+        for (int i = 0; i < DW; ++i) span_acc(w[gidx * DW + i], mx, mn);
+        uint32_t a = lane_pack(mx, true), b = lane_pack(mn, false);
+        if constexpr (G == 256) {
+          uint32_t t = dpp_u32<kQuadXor1>(a); a = a > t ? a : t;
+          t = dpp_u32<kQuadXor2>(a); a = a > t ? a : t;
+          t = dpp_u32<kQuadXor1>(b); b = b < t ? b : t;
+          t = dpp_u32<kQuadXor2>(b); b = b < t ? b : t;
+        }
+        flagged |= group_span(a, b) > kMaxSpan;
+      }
+    }
+
+    // ---- widen, transform ----
+    double v[CH];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[2 * i] = (double)bf16lo(w[i]);
+      v[2 * i + 1] = (double)bf16hi(w[i]);
+    }
+    fwht_inlane<G, CH>(v);
+    if constexpr (G == 256) {
+      const int q = c & 3;  // position of this lane's 64-element part in its group
+      const double s1 = (q & 1) ? -1.0 : 1.0;
+      const double s2 = (q & 2) ? -1.0 : 1.0;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s1, dpp_f64<kQuadXor1>(v[i]));
+#pragma unroll
+      for (int i = 0; i < CH; ++i) v[i] = __builtin_fma(v[i], s2, dpp_f64<kQuadXor2>(v[i]));
+    }
+
+    // u = RN32(y) (y = unscaled, unsigned sum); x_r = d_j * u * 2^-k for normal x_r
+    float u[CH];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      u[i] = (float)v[i];
+      amax = fmaxf(amax, fabsf(u[i]));
+    }
+
+    const int slot = it % 3;
+    if (active) {
+      atomicMax(&s_rowmax[slot][r_in], __float_as_uint(amax));
+      if (flagged) atomicOr(&s_rowflag[slot][r_in], 1u);
+    }
+    __syncthreads();
+    if (tid < rows_per_block) {
+      const int nslot = (it + 2) % 3;
+      s_rowmax[nslot][tid] = 0u;
+      s_rowflag[nslot][tid] = 0u;
+    }
+
+    if (active) {
+      const float amax_u = __uint_as_float(s_rowmax[slot][r_in]);
+      const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact unless deferred
+      const bool deferred = s_rowflag[slot][r_in] != 0u || !(amax_u <= 3.0e38f) ||
+                            (amax_u > 0.0f && amax_x < 0x1p-100f);
+      if (deferred) {
+        if (c == 0) scale[row] = __uint_as_float(kDeferredRow);
+      } else {
+        float sc, inv_u;
+        if (amax_u > 0.0f) {
+          sc = amax_x / 127.0f;
+          const float inv = 127.0f / amax_x;
+          inv_u = inv * (1.0f / (float)(1 << KS));
+        } else {
+          sc = 0.0f;
+          inv_u = 0.0f;
+        }
+        if (c == 0) scale[row] = sc;
+
+        uint32_t outw[16];
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+          uint32_t b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = u[4 * d + e] * inv_u;
+            b[e] = __float_as_uint(p + kQuantBias);  // q + 128 in the low byte
+          }
+          const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+          const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+          const uint32_t packed = t0 | t1;
+          const uint32_t nib = ((d < 8 ? sg0 : sg1) >> ((4 * d) & 31)) & 0xFu;
+          const uint32_t m = nibble_to_bytemask(nib);
+          // negate the bytes with d = -1 (biased: 256 - v never carries), unbias
+          outw[d] = ((packed ^ m) + (m & 0x01010101u)) ^ 0x80808080u;
+        }
+        u4* o = reinterpret_cast<u4*>(xq + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = (u4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = wn[i];
+  }
 }
 
 // ============================================================================
@@ -286,7 +316,7 @@ template <int G>
 __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
     uint32_t* __restrict__ tensor_amax, int64_t rows, int K, int T, int rows_per_block,
-    SignMask sm, int mode) {
+    int64_t nbatches, SignMask sm, int mode) {
   constexpr int CH = 32;
   constexpr int LOGG = ilog2(G);
   constexpr int KS = LOGG / 2;
@@ -299,7 +329,24 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   const int tid = threadIdx.x;
   const int r_in = tid / T;
   const int c = tid - r_in * T;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_block + r_in;
+  if (mode == kRowDeferred) {
+    // one parallel look at the scale slots of all rows this block would
+    // visit; usually none is deferred and the block is done
+    bool any = false;
+    const int64_t per_pass = (int64_t)gridDim.x * rows_per_block;
+    for (int64_t i = tid; ; i += blockDim.x) {
+      const int64_t pass = i / rows_per_block;
+      const int64_t r = (int64_t)blockIdx.x * rows_per_block + pass * per_pass +
+                        (i - pass * rows_per_block);
+      if (r >= rows) break;
+      any |= __float_as_uint(scale[r]) == kDeferredRow;
+    }
+    if (__syncthreads_or(any) == 0) return;
+  }
+  // persistent grid: batches of rows_per_block rows, strided by gridDim.x
+  for (int64_t batch = blockIdx.x; batch < nbatches; batch += gridDim.x) {
+  __syncthreads();  // the previous batch's readers of the LDS slots are done
+  const int64_t row = batch * rows_per_block + r_in;
   bool active = (r_in < rows_per_block) && (row < rows);
   if (tid < rows_per_block) {
     s_rowmax[tid] = 0u;
@@ -308,10 +355,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   if (mode == kRowDeferred) {
     // rows that the fast kernel finished are skipped as a whole
     if (active) active = __float_as_uint(scale[row]) == kDeferredRow;
-    __syncthreads();
-    if (active && c == 0) s_rowflag[r_in] = 1u;
-    __syncthreads();
-    if (__syncthreads_or(active) == 0) return;
+    if (__syncthreads_or(active) == 0) continue;
   }
 
   uint32_t w[16];
@@ -419,7 +463,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     if ((tid & 63) == 0 && amax > 0.0f) atomicMax(tensor_amax, __float_as_uint(amax));
-    return;
+    continue;
   }
 
   float rmax;
@@ -431,7 +475,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     __syncthreads();
     rmax = __uint_as_float(s_rowmax[r_in]);
   }
-  if (!active) return;
+  if (!active) continue;
 
   float s = 0.0f, inv = 0.0f, pre = 1.0f;
   if (rmax > 0.0f) {
@@ -462,6 +506,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
 #pragma unroll
   for (int i = 0; i < CH / 16; ++i)
     o[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
+  }  // batch loop
 }
 
 __global__ void tensor_scale_init_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
@@ -503,23 +548,41 @@ TeamShape team_shape(int T) {
   return best;
 }
 
+// Resident waves per CU that the persistent fast kernel aims for
+// (compile-time tunable).
+#ifndef CONVROT_FAST_WAVES_PER_CU
+#define CONVROT_FAST_WAVES_PER_CU 8
+#endif
+constexpr int kFastWavesPerCU = CONVROT_FAST_WAVES_PER_CU;
+
 template <int G>
 hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
                        const SignMask& sm, hipStream_t st) {
   const TeamShape ts = team_shape(K / 64);
-  const int64_t blocks = (rows + ts.rpb - 1) / ts.rpb;
+  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
+  const int64_t cap = (int64_t)kNumCUs * kFastWavesPerCU / (ts.block / 64);
+  const int64_t blocks = nbatches < cap ? nbatches : cap;
   hipLaunchKernelGGL(rotate_quant_fast_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0, st,
-                     x, xq, s, rows, K, ts.T, ts.rpb, sm);
+                     x, xq, s, rows, K, ts.T, ts.rpb, nbatches, sm);
   return hipGetLastError();
 }
+
+// Resident waves per CU of the persistent exact kernel. Over the rows the
+// fast kernel deferred (usually none) a small grid scans the scale slots.
+constexpr int kExactWavesPerCU = 8;
+constexpr int kDeferredWavesPerCU = 2;
 
 template <int G>
 hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,
                         int64_t rows, int K, const SignMask& sm, int mode, hipStream_t st) {
   const TeamShape ts = team_shape(K / 32);
-  const int64_t blocks = (rows + ts.rpb - 1) / ts.rpb;
+  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
+  const int wpc = mode == kRowDeferred ? kDeferredWavesPerCU : kExactWavesPerCU;
+  int64_t cap = (int64_t)kNumCUs * wpc / (ts.block / 64);
+  if (cap < 1) cap = 1;
+  const int64_t blocks = nbatches < cap ? nbatches : cap;
   hipLaunchKernelGGL(rotate_quant_exact_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0,
-                     st, x, xq, s, tensor_amax, rows, K, ts.T, ts.rpb, sm, mode);
+                     st, x, xq, s, tensor_amax, rows, K, ts.T, ts.rpb, nbatches, sm, mode);
   return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@
  *     is enqueued and no output is touched.
  *   - Shapes: K % 64 == 0, K % g == 0, K <= 16384 for the rotating entry points;
  *     N % 16 == 0 and K <= 133144 (int32 accumulator bound) for the GEMM;
- *     all dimensions < 2^31. M == 0 is a no-op (the M-sized buffers may then
- *     be null).
+ *     all dimensions < 2^31, and ceil(M/128) * ceil(N/128) < 2^31 for the
+ *     GEMM. M == 0 is a no-op (the M-sized buffers may then be null).
  *   - Alignment: tensor base pointers 16-byte aligned, scales 4-byte aligned.
  *   - Results are bit-identical from run to run and independent of slicing.
  */

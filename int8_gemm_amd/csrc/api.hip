@@ -93,6 +93,10 @@ convrot_status check_gemm(const char* fn, int64_t m, int64_t n, int64_t k) {
     return fail(CONVROT_E_UNSUPPORTED_SHAPE,
                 "%s: need k %% 64 == 0, n %% 16 == 0, k <= %lld (m=%lld n=%lld k=%lld)", fn,
                 (long long)kMaxGemmK, (long long)m, (long long)n, (long long)k);
+  // the smallest block tile is 128 x 128: the tile count must fit the 32-bit grid
+  if (((m + 127) / 128) * ((n + 127) / 128) >= kMaxDim)
+    return fail(CONVROT_E_UNSUPPORTED_SHAPE, "%s: output too large (m=%lld n=%lld)", fn,
+                (long long)m, (long long)n);
   return CONVROT_OK;
 }
 

@@ -108,8 +108,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   // ---- per-lane DMA sources: instruction t of this wave covers combined
   // rows RPI*q .. RPI*q+RPI-1 (weights first, then activations); lane ->
   // row RPI*q + lane/CPR, 16-byte chunk lane%CPR (whole L2 lines for BK=128) ----
-  // 32-bit byte offsets (host keeps M*K and N*K below 2^31); the region
-  // base pointer and the K-step offset go in SGPRs
+  // 32-bit byte offsets from the tile's first weight / activation row
+  // (below BM*K <= 256 * 133144 < 2^31); the 64-bit tile base pointer and the
+  // K-step offset go in SGPRs. Rows past the matrix edge re-read its last row.
+  const int8_t* wtile = wq + (int64_t)n0 * K;
+  const int8_t* xtile = xq + (int64_t)m0 * K;
   uint32_t voff[LW];
   bool is_w[LW];
   int ldsoff[LW];
@@ -120,10 +123,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
     const int p = lane % CPR;
     is_w[t] = (RPI * q) < BN;  // whole instruction in one region (BN % RPI == 0)
     if (row < BN) {
-      const int n = min(n0 + row, N - 1);
+      const int n = min(n0 + row, N - 1) - n0;
       voff[t] = (uint32_t)n * (uint32_t)K + 16u * p;
     } else {
-      const int m = min(m0 + row - BN, M - 1);
+      const int m = min(m0 + row - BN, M - 1) - m0;
       voff[t] = (uint32_t)m * (uint32_t)K + 16u * p;
     }
     ldsoff[t] = q * 1024;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   auto issue = [&](int s, int slot) {
 #pragma unroll
     for (int t = 0; t < LW; ++t) {
-      const int8_t* base = uniform_ptr((is_w[t] ? wq : xq) + (int64_t)s * BK);
+      const int8_t* base = uniform_ptr((is_w[t] ? wtile : xtile) + (int64_t)s * BK);
       const uint32_t dst =
           __builtin_amdgcn_readfirstlane(lds_u32 + (uint32_t)(slot * STAGE + ldsoff[t]));
       dma16(base, voff[t], dst);

@@ -87,6 +87,10 @@ def test_null_and_misaligned_and_overlap(lib):
     # gemm: no output at all
     assert _status(lib, "convrot_gemm_int8", FAKE, FAKE, FAKE, FAKE, None, 8, 16, 64, None,
                    None, None) == 1
+    # gemm: more output tiles than a 32-bit grid holds
+    assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 1 << 30, 1 << 30,
+                   64, ctypes.c_void_p(1 << 28), None, None) == 3
     # gemm: n % 16, k % 64
     assert _status(lib, "convrot_gemm_int8", FAKE, ctypes.c_void_p(1 << 22),
                    ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 8, 24, 64,

@@ -7,19 +7,25 @@
 // "int8 Compute", introduction: the input is quantized per token and int8 is
 // multiplied by int8); the pages run it through Triton on NVIDIA, this is a
 // gfx950 design of its own:
-//   * block tile BM x BN (templated: 256x256 with 8 waves in a 2 x 4 grid,
-//     192x192 and 128x128 with 4 waves in a 2 x 2 grid); v_mfma_i32_32x32x32_i8 (on gfx950 it sustains the full int8
-//     rate, while the 16x16x64 form sustains about half) with the weight rows
-//     in the A operand, so each lane's accumulators come in runs of 4
-//     consecutive output columns;
-//   * K-step BK = 64 bytes (a 128-byte step measured slower: fewer stages fit
-//     in LDS, so fewer bytes are in flight); an NS-deep ring of LDS stages filled by
-//     global_load_lds_dwordx4 (global -> LDS without VGPRs); one barrier per
-//     K-step; the loads for step s+NS-1 are issued right after that barrier;
-//   * LDS stage layout: row-major rows of BK bytes, weights then
-//     activations; each DMA instruction fills 1024 / BK rows (1 KB);
+//   * block tile BM x BN: 256x256 with 8 compute waves in a 2 x 4 grid,
+//     192x192 with 4 compute waves (2 x 2) plus 2 producer waves, 128x128
+//     with 4 waves (2 x 2, two blocks per CU); v_mfma_i32_32x32x32_i8 (on
+//     gfx950 it sustains the full int8 rate, the 16x16x64 form about half)
+//     with the weight rows in the A operand, so each lane's accumulators
+//     come in runs of 4 consecutive output columns;
+//   * K-step BK = 64 bytes; an NS-deep ring of LDS stages filled by
+//     global_load_lds_dwordx4 (global -> LDS, no VGPRs); one barrier per
+//     K-step; the copies of step s+NS-1 are issued right after it. With
+//     producer waves, only they issue copies and wait for them;
+//   * LDS stage: rows of 64 B, weights then activations; each copy
+//     instruction fills 16 rows (1 KB); within a row the 16-byte chunks are
+//     XOR-swizzled by (row >> 2) & 3, which makes the fragment reads free of
+//     bank conflicts;
 //   * the block index is remapped so that each of the 8 XCDs gets a
 //     contiguous range of tiles, walked in groups of 8 tile rows (L2 reuse).
+// Measured on MI355X: a 128-byte K-step, deeper rings, an L2 prefetch copy
+// and non-temporal output stores were all slower; the K-loop is bound by
+// the rate at which the copies stream operands from L2/MALL into LDS.
 // Both operands are K-contiguous ("TN"). K % 64 == 0, N % 16 == 0.
 
 #include "common.h"
@@ -61,8 +67,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB>
-__global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP>
+__global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_x, const int8_t* __restrict__ wq,
     const float* __restrict__ s_w, const uint16_t* __restrict__ bias, int M, int N, int K,
     int tiles_m, int tiles_n, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
@@ -72,10 +78,17 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   constexpr int STAGE = (BM + BN) * BK;         // bytes per LDS stage
   constexpr int RPI = 1024 / BK;                // rows per 1 KB DMA instruction
   constexpr int CPR = BK / 16;                  // 16-byte chunks per row
-  constexpr int LW = (BM + BN) / (RPI * NW);    // DMA instructions per wave per stage
+  // NP == 0: every wave copies its share of each stage and computes.
+  // NP > 0: NP extra producer waves issue all copies and wait for them, so
+  // a stalled copy issue never holds up a compute wave's MFMAs; the compute
+  // (consumer) waves only read LDS and multiply. Both meet at the one
+  // barrier per K-step.
+  constexpr int DW = NP > 0 ? NP : NW;          // waves that issue copies
+  constexpr int LW = (BM + BN) / (RPI * DW);    // DMA instructions per copying wave per stage
   constexpr int H = BK / 32;                    // 32-k slices per K-step
-  static_assert(BK == 64 || BK == 128, "K-step");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * NW) == 0, "tile shape");
+  static_assert(BK == 64, "K-step (the LDS swizzle assumes 4 chunks per row)");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * DW) == 0, "tile shape");
+  static_assert((NS - 1) * LW < 64, "copies in flight per wave must fit vmcnt");
   static_assert(NS >= 3, "the K-loop waits for stage s+1 before issuing stage s+NS-1");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -84,6 +97,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   const int wave = tid >> 6;
   const int wn = wave % WN;
   const int wm = wave / WN;
+  const int cw = NP > 0 ? wave - NW : wave;  // index among the copying waves
 
   // ---- tile index: XCD-contiguous ranges, grouped rows ----
   const int ntiles = tiles_m * tiles_n;
@@ -118,19 +132,22 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   int ldsoff[LW];
 #pragma unroll
   for (int t = 0; t < LW; ++t) {
-    const int q = wave * LW + t;
+    const int q = (cw > 0 ? cw : 0) * LW + t;  // consumers of a producer layout never copy
     const int row = RPI * q + lane / CPR;
     const int p = lane % CPR;
     is_w[t] = (RPI * q) < BN;  // whole instruction in one region (BN % RPI == 0)
+    // LDS slot p of the row holds global chunk p ^ swz(row) (bank swizzle)
+    const uint32_t chunk = (uint32_t)(p ^ ((row >> 2) & 3));
     if (row < BN) {
       const int n = min(n0 + row, N - 1) - n0;
-      voff[t] = (uint32_t)n * (uint32_t)K + 16u * p;
+      voff[t] = (uint32_t)n * (uint32_t)K + 16u * chunk;
     } else {
       const int m = min(m0 + row - BN, M - 1) - m0;
-      voff[t] = (uint32_t)m * (uint32_t)K + 16u * p;
+      voff[t] = (uint32_t)m * (uint32_t)K + 16u * chunk;
     }
     ldsoff[t] = q * 1024;
   }
+  const int nk = K / BK;
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
   // wave-uniform operands of the DMA go through readfirstlane into SGPRs
   auto uniform_ptr = [](const int8_t* p) {
@@ -155,20 +172,62 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (v16i){};
 
-  const int nk = K / BK;
+  // a stage's copies are complete when at most the copies of the p later
+  // stages are outstanding (copies complete in order)
+  auto wait_stage_runtime = [&](int p) {  // p = later stages allowed to stay pending
+    if (p >= NS - 2) {
+      wait_vmcnt<(NS - 2) * LW>();
+    } else if (p == 3) {
+      wait_vmcnt<3 * LW>();
+    } else if (p == 2) {
+      wait_vmcnt<2 * LW>();
+    } else if (p == 1) {
+      wait_vmcnt<LW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+
+  if constexpr (NP > 0) {
+    if (wave >= NW) {
+      // ---- producer: stage s+1 landed before the barrier that ends step
+      // s; after it, the slot of stage s-1 (read by every consumer before
+      // that barrier) takes stage s+NS-1. Same barrier count as a consumer.
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s, s);
+      wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
+      lds_barrier();
+      for (int s = 0; s + 1 < nk; ++s) {
+        wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
+        lds_barrier();
+        if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
+      }
+      return;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(s, s);
+  }
 
   // 32x32x32 operands: lane -> row lane%32 of a 32-row block, 16-byte
   // half lane/32 of the 32-byte k-slice h of the K-step
   const int fr = lane & 31;
   const int fh = lane >> 5;
+  // Row r of a stage keeps its 16-byte chunk c in slot c ^ swz(r), with
+  // swz(r) = (r >> 2) & 3: the 16 lanes that read 16 consecutive rows at one
+  // chunk then hit 16 distinct 4-bank groups (with plain 64-byte rows, rows
+  // r and r + 4 share banks). Row blocks start at multiples of 32, so
+  // swz(row) = (fr >> 2) & 3 for every fragment of this lane.
+  const int swz = (fr >> 2) & 3;
+  const int dsw0 = 16 * (fh ^ swz);        // chunk fh of slice 0
+  const int dsw1 = 16 * ((2 + fh) ^ swz);  // chunk 2 + fh of slice 1
   int aoff[NI], boff[NJ];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) aoff[i] = (wn * WTN + i * 32 + fr) * BK + 16 * fh;
+  for (int i = 0; i < NI; ++i) aoff[i] = (wn * WTN + i * 32 + fr) * BK;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) boff[j] = BN * BK + (wm * WTM + j * 32 + fr) * BK + 16 * fh;
+  for (int j = 0; j < NJ; ++j) boff[j] = BN * BK + (wm * WTM + j * 32 + fr) * BK;
 
   // Each K-step is H 32-k slices whose fragments alternate between two
   // register sets X (even slices) and Y (odd slices): while the MFMAs of one
@@ -179,7 +238,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   constexpr int NF = NI + NJ;
   v4i xa[NI], xb[NJ], ya[NI], yb[NJ];
   auto read_slice = [&](int s, int h, v4i (&fa)[NI], v4i (&fb)[NJ]) {
-    const uint8_t* base = lds + (s % NS) * STAGE + 32 * h;
+    const uint8_t* base = lds + (s % NS) * STAGE + (h == 0 ? dsw0 : dsw1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[j] = *reinterpret_cast<const v4i*>(base + boff[j]);
 #pragma unroll
@@ -205,19 +264,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
     __builtin_amdgcn_sched_group_barrier(0x100, NF - NR, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
   };
-  auto wait_stage_runtime = [&](int p) {  // p = later stages allowed to stay pending
-    if (p >= NS - 2) {
-      wait_vmcnt<(NS - 2) * LW>();
-    } else if (p == 3) {
-      wait_vmcnt<3 * LW>();
-    } else if (p == 2) {
-      wait_vmcnt<2 * LW>();
-    } else if (p == 1) {
-      wait_vmcnt<LW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  };
   // the first H-1 slices of step s (slice 0 is already in X)
   auto early_slices = [&](int s) {
 #pragma unroll
@@ -233,16 +279,33 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
     }
   };
 
-  wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
+  // Consume the epilogue's pointer arguments here: their scalar loads then
+  // complete before the K-loop. A scalar load still in flight at the loop
+  // entry (they return out of order) makes every LDS-read wait in the loop
+  // a full lgkmcnt(0) drain.
+  asm volatile("" ::"s"(y), "s"(acc_out), "s"(s_x), "s"(s_w), "s"(bias));
+  if constexpr (NP == 0) wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
   lds_barrier();
   read_slice(0, 0, xa, xb);
-  const int steady = nk - (NS - 1);  // steps that also refill the ring
-  int s = 0;
+  if constexpr (NP > 0) {
+    // consumer of a producer layout: no copies, no waits, one uniform loop
+    for (int s = 0; s < nk; ++s) {
+      early_slices(s);
+      if (s + 1 < nk) {
+        lds_barrier();
+        read_slice(s + 1, 0, xa, xb);
+      }
+      mfma_slice(ya, yb);
+      sched_slice();
+    }
+  }
+  const int steady = NP > 0 ? 0 : nk - (NS - 1);  // steps that also refill the ring
+  int s = NP > 0 ? nk : 0;
   for (; s < steady; ++s) {
     early_slices(s);
-    wait_vmcnt<(NS - 3) * LW>();  // stage s+1 landed (stage s+NS-2 may be pending)
+    if constexpr (NP == 0) wait_vmcnt<(NS - 3) * LW>();  // stage s+1 landed
     lds_barrier();
-    issue(s + NS - 1, (s + NS - 1) % NS);
+    if constexpr (NP == 0) issue(s + NS - 1, (s + NS - 1) % NS);
     read_slice(s + 1, 0, xa, xb);
     mfma_slice(ya, yb);  // H is even: the last slice sits in Y
     sched_slice();
@@ -250,7 +313,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_i8_kernel(
   for (; s < nk; ++s) {
     early_slices(s);
     if (s + 1 < nk) {
-      wait_stage_runtime(nk - 2 - s);
+      if constexpr (NP == 0) wait_stage_runtime(nk - 2 - s);
       lds_barrier();
       read_slice(s + 1, 0, xa, xb);
       mfma_slice(ya, yb);
@@ -305,13 +368,13 @@ struct TileCfg {
   int bm, bn, ns, per_cu;
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB>
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
 hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                       const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
                       hipStream_t st) {
   constexpr int lds_bytes = NS * (BM + BN) * BK;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
-  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB>;
+  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP>;
   static bool attr = false;  // benign race: the call is idempotent
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -321,7 +384,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
   }
   const int tiles_m = (m + BM - 1) / BM;
   const int tiles_n = (n + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(64 * WM * WN), lds_bytes, st, xq, s_x, wq, s_w,
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(64 * (WM * WN + NP)), lds_bytes, st, xq, s_x, wq, s_w,
                      bias, m, n, k, tiles_m, tiles_n, y, acc);
   return hipGetLastError();
 }
@@ -358,7 +421,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, con
   if (t.bm == 256)
     return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
   if (t.bm == 192)
-    return launch_cfg<192, 192, 64, 2, 2, 6, 1>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+    return launch_cfg<192, 192, 64, 2, 2, 6, 1, 2>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
   return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
 }
 
@@ -372,7 +435,7 @@ hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq
     case 256:
       return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
     case 192:
-      return launch_cfg<192, 192, 64, 2, 2, 6, 1>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
+      return launch_cfg<192, 192, 64, 2, 2, 6, 1, 2>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
     default:
       return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
   }

@@ -287,40 +287,22 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   if constexpr (NP == 0) wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
   lds_barrier();
   read_slice(0, 0, xa, xb);
-  if constexpr (NP > 0) {
-    // consumer of a producer layout: no copies, no waits, one uniform loop
-    for (int s = 0; s < nk; ++s) {
-      early_slices(s);
-      if (s + 1 < nk) {
-        lds_barrier();
-        read_slice(s + 1, 0, xa, xb);
-      }
-      mfma_slice(ya, yb);
-      sched_slice();
-    }
-  }
-  const int steady = NP > 0 ? 0 : nk - (NS - 1);  // steps that also refill the ring
-  int s = NP > 0 ? nk : 0;
-  for (; s < steady; ++s) {
-    early_slices(s);
-    if constexpr (NP == 0) wait_vmcnt<(NS - 3) * LW>();  // stage s+1 landed
-    lds_barrier();
-    if constexpr (NP == 0) issue(s + NS - 1, (s + NS - 1) % NS);
-    read_slice(s + 1, 0, xa, xb);
-    mfma_slice(ya, yb);  // H is even: the last slice sits in Y
-    sched_slice();
-  }
-  for (; s < nk; ++s) {
+  // One uniform loop (no separate tail copy, which would double the live
+  // ranges): before the last slice of step s, stage s+1 must have landed;
+  // the barrier publishes it and frees the slot of stage s-1 for the copies
+  // of stage s+NS-1.
+  for (int s = 0; s < nk; ++s) {
     early_slices(s);
     if (s + 1 < nk) {
-      if constexpr (NP == 0) wait_stage_runtime(nk - 2 - s);
+      if constexpr (NP == 0) wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
       lds_barrier();
+      if constexpr (NP == 0) {
+        if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
+      }
       read_slice(s + 1, 0, xa, xb);
-      mfma_slice(ya, yb);
-      sched_slice();
-    } else {
-      mfma_slice(ya, yb);
     }
+    mfma_slice(ya, yb);  // H is even: the last slice sits in Y
+    sched_slice();
   }
 
   // ---- epilogue: 32x32 output layout: lane holds m = lane % 32 of the

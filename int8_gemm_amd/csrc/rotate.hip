@@ -568,9 +568,12 @@ hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, in
 }
 
 // Resident waves per CU of the persistent exact kernel. Over the rows the
-// fast kernel deferred (usually none) a small grid scans the scale slots.
+// fast kernel deferred, each block first scans its rows' scale slots in one
+// parallel pass and returns at once when none is deferred, so a full grid
+// costs little on ordinary inputs and keeps the chip busy on inputs (GELU
+// tails) that defer most rows.
 constexpr int kExactWavesPerCU = 8;
-constexpr int kDeferredWavesPerCU = 2;
+constexpr int kDeferredWavesPerCU = 8;
 
 template <int G>
 hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,

@@ -57,12 +57,32 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
                                                       const float* __restrict__ s_w,
                                                       int64_t nrows, SignMask sm,
                                                       uint16_t* __restrict__ out) {
-  constexpr int R = G > 32 ? G : 32;  // bytes per view row
-  constexpr int NB = R / 32;          // 32-blocks per view row
+  constexpr int R = G > 32 ? G : 32;   // bytes per view row
+  constexpr int NB = R / 32;           // 32-blocks per view row
   constexpr int KS = ilog2(G) / 2;
-  const int lane = threadIdx.x & 63;
-  const uint32_t jl = lane & 31;      // A row (output j within a 32-block)
-  const uint32_t kh = lane >> 5;      // k-slice: il = 16*kh + b
+  // A block takes 4 tiles of 32 view rows, or one tile whose 8 output
+  // 32-blocks are spread over its 4 waves (g = 256): a contiguous chunk of
+  // CHUNK input bytes, loaded coalesced into LDS and prefetched one chunk
+  // ahead through registers.
+  constexpr int NQ = NB >= 4 ? 4 : 1;      // waves per tile
+  constexpr int JW = NB / NQ;              // output 32-blocks per wave
+  constexpr int TPB = 4 / NQ;              // tiles per block
+  constexpr int CHUNK = TPB * 32 * R;      // input bytes per block step (<= 8 KB)
+  constexpr int NLD = CHUNK / (256 * 16);  // 16-byte loads per thread per chunk
+  static_assert(CHUNK % (256 * 16) == 0 || CHUNK < 256 * 16, "chunk");
+  constexpr int LR = R + 16;               // LDS bytes per staged input row (padded)
+  constexpr int OW = JW * 32;              // outputs per row per wave
+  constexpr int OSTR = OW * 2 + 16;        // LDS bytes per staged output row (padded)
+  __shared__ __attribute__((aligned(16))) uint8_t s_in[TPB * 32 * LR];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[4][32 * OSTR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const uint32_t jl = lane & 31;  // A row (output j within a 32-block) / B column (view row)
+  const uint32_t kh = lane >> 5;  // k-slice: il = 16*kh + b
+  const int tl = wave / NQ;       // tile of this wave within the chunk
+  const int jq = wave % NQ;       // its share of the output 32-blocks
 
   // ---- A fragments ----
   v4i fragP[NB], fragN[NB];
@@ -92,25 +112,44 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
   }
 
   const float c = *s_w * (1.0f / (float)(1 << KS));
-  // work item = (32-row tile, JW consecutive output 32-blocks): the NB*NB
-  // MFMAs of a tile are spread over NB/JW waves (the tile's input bytes are
-  // re-read from L2 by each), which shortens each wave's serial MFMA chain.
-  constexpr int JW = NB < 2 ? NB : 2;
-  constexpr int NQ = NB / JW;
-  const int64_t nitems = (nrows + 31) / 32 * NQ;
-  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t wstride = (int64_t)gridDim.x * 4;
+  const int64_t ntiles = (nrows + 31) / 32;
+  const int64_t nchunks = (ntiles + TPB - 1) / TPB;
+  const int64_t in_bytes = nrows * R;
 
-  for (int64_t item = wave0; item < nitems; item += wstride) {
-    const int64_t tile = item / NQ;
-    const int jq = (int)(item % NQ);
-    const int64_t r = tile * 32 + jl;                   // B column = this lane's view row
-    const int64_t rr = r < nrows ? r : nrows - 1;
+  // coalesced chunk load: thread tid takes 16-byte pieces tid, tid + 256, ...
+  // (bytes past the end read as zero)
+  auto load_chunk = [&](int64_t ch, u4 (&r)[NLD > 0 ? NLD : 1]) {
+#pragma unroll
+    for (int i = 0; i < (NLD > 0 ? NLD : 1); ++i) {
+      const int off = (tid + 256 * i) * 16;
+      const int64_t g = ch * CHUNK + off;
+      r[i] = (ch < nchunks && off < CHUNK && g < in_bytes)
+                 ? *reinterpret_cast<const u4*>(wq + g)
+                 : (u4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_chunk = [&](const u4 (&r)[NLD > 0 ? NLD : 1]) {
+#pragma unroll
+    for (int i = 0; i < (NLD > 0 ? NLD : 1); ++i) {
+      const int off = (tid + 256 * i) * 16;
+      if (off < CHUNK) *reinterpret_cast<u4*>(s_in + off / R * LR + off % R) = r[i];
+    }
+  };
+
+  u4 pre[NLD > 0 ? NLD : 1];
+  int64_t ch = blockIdx.x;
+  load_chunk(ch, pre);
+  store_chunk(pre);
+  __syncthreads();
+  for (; ch < nchunks; ch += gridDim.x) {
+    load_chunk(ch + gridDim.x, pre);  // next chunk, in flight during this one
+
+    const int64_t tile = ch * TPB + tl;
     v4i bfr[NB];
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
-      bfr[ib] = *reinterpret_cast<const v4i*>(wq + rr * R + 32 * ib + 16 * kh);
-    const bool ok = r < nrows;
+      bfr[ib] = *reinterpret_cast<const v4i*>(s_in + (tl * 32 + jl) * LR + 32 * ib + 16 * kh);
+    uint8_t* so = s_out[wave];
 #pragma unroll
     for (int jw = 0; jw < JW; ++jw) {
       const int jb = jq * JW + jw;
@@ -121,31 +160,36 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
         acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(negb ? fragN[ib] : fragP[ib], bfr[ib], acc,
                                                      0, 0, 0);
       }
-      // lane (jl, kh) holds outputs j = 8a + 4kh + e of view row r; pack to
-      // bf16 pairs, then swap halves with lane jl + 32 (v_permlane32_swap) so
-      // that lane kh = 0 holds j = 16h .. 16h+7 and lane kh = 1 holds
-      // j = 16h+8 .. 16h+15 for h = 0, 1: two 16-byte stores per lane.
-      uint32_t pk[4][2];
+      // lane (jl, kh) holds outputs j = 8a + 4kh + e of view row jl: stage
+      // them as bf16 in this wave's LDS rows
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        pk[a][0] = pack_bf16x2((float)acc[4 * a + 0] * c, (float)acc[4 * a + 1] * c);
-        pk[a][1] = pack_bf16x2((float)acc[4 * a + 2] * c, (float)acc[4 * a + 3] * c);
-      }
-      uint16_t* o = out + r * R + 32 * jb + 8 * kh;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u4 v;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          // swap lanes 32..63 of pk[2h] with lanes 0..31 of pk[2h+1]
-          const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * h][e], pk[2 * h + 1][e],
-                                                           false, false);
-          v[e] = sw[0];      // kh = 0: own a = 2h; kh = 1: partner's a = 2h+1
-          v[2 + e] = sw[1];  // kh = 0: partner's a = 2h; kh = 1: own a = 2h+1
-        }
-        if (ok) *reinterpret_cast<u4*>(o + 16 * h) = v;
+        const u2 v = {pack_bf16x2((float)acc[4 * a + 0] * c, (float)acc[4 * a + 1] * c),
+                      pack_bf16x2((float)acc[4 * a + 2] * c, (float)acc[4 * a + 3] * c)};
+        *reinterpret_cast<u2*>(so + jl * OSTR + 2 * (32 * jw + 8 * a + 4 * kh)) = v;
       }
     }
+    // (LDS ops of one wave complete in order; keep the compiler from
+    // moving the reads below above the writes above)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // coalesced stores: each row's OW outputs are contiguous in the output;
+    // lane -> (row, 16-byte piece)
+    constexpr int PPR = OW * 2 / 16;  // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;     // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / PPR;
+      const int pc = lane % PPR;
+      const u4 v = *reinterpret_cast<const u4*>(so + row * OSTR + 16 * pc);
+      const int64_t vr = tile * 32 + row;
+      if (vr < nrows)
+        *reinterpret_cast<u4*>(out + vr * R + jq * OW + 8 * pc) = v;
+    }
+    __syncthreads();  // every wave is done with s_in and its own s_out
+    store_chunk(pre);
+    __syncthreads();
   }
 }
 
@@ -157,10 +201,14 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t
   if (ne == 0) return hipSuccess;
   const int R = g > 32 ? g : 32;
   const int64_t nrows = ne / R;
-  const int64_t items = (nrows + 31) / 32 * (R >= 64 ? R / 64 : 1);
-  int64_t blocks = (items + 3) / 4;
-  const int64_t cap = 256 * 8;
-  if (blocks > cap) blocks = cap;
+  const int64_t tiles = (nrows + 31) / 32;
+  const int tpb = (R / 32 >= 4) ? 1 : 4;  // tiles per block step
+  const int64_t chunks = (tiles + tpb - 1) / tpb;
+#ifndef CONVROT_DEQUANT_BLOCKS_PER_CU
+#define CONVROT_DEQUANT_BLOCKS_PER_CU 4
+#endif
+  const int64_t cap = (int64_t)kNumCUs * CONVROT_DEQUANT_BLOCKS_PER_CU;  // persistent blocks
+  const int64_t blocks = chunks < cap ? chunks : cap;
   switch (g) {
     case 4:
       hipLaunchKernelGGL(dequant_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w,

@@ -8,24 +8,30 @@
 // multiplied by int8); the pages run it through Triton on NVIDIA, this is a
 // gfx950 design of its own:
 //   * block tile BM x BN: 256x256 with 8 compute waves in a 2 x 4 grid,
-//     192x192 with 4 compute waves (2 x 2) plus 2 producer waves, 128x128
+//     192x192 with 4 compute waves (2 x 2) plus 4 producer waves, 128x128
 //     with 4 waves (2 x 2, two blocks per CU); v_mfma_i32_32x32x32_i8 (on
 //     gfx950 it sustains the full int8 rate, the 16x16x64 form about half)
 //     with the weight rows in the A operand, so each lane's accumulators
 //     come in runs of 4 consecutive output columns;
-//   * K-step BK = 64 bytes; an NS-deep ring of LDS stages filled by
-//     global_load_lds_dwordx4 (global -> LDS, no VGPRs); one barrier per
-//     K-step; the copies of step s+NS-1 are issued right after it. With
-//     producer waves, only they issue copies and wait for them;
-//   * LDS stage: rows of 64 B, weights then activations; each copy
-//     instruction fills 16 rows (1 KB); within a row the 16-byte chunks are
-//     XOR-swizzled by (row >> 2) & 3, which makes the fragment reads free of
+//   * K-step BK = 64 bytes, or 128 for the 192 tile when K allows; an
+//     NS-deep ring of LDS stages filled by global_load_lds_dwordx4 (global
+//     -> LDS, no VGPRs); one barrier per K-step; the copies of step s+NS-1
+//     are issued right after it. With producer waves, only they issue
+//     copies and wait for them;
+//   * LDS stage: rows of BK bytes, weights then activations; each copy
+//     instruction fills 1024 / BK rows; within a row the 16-byte chunks are
+//     XOR-swizzled by row (below), which makes the fragment reads free of
 //     bank conflicts;
 //   * the block index is remapped so that each of the 8 XCDs gets a
 //     contiguous range of tiles, walked in groups of 8 tile rows (L2 reuse).
-// Measured on MI355X: a 128-byte K-step, deeper rings, an L2 prefetch copy
-// and non-temporal output stores were all slower; the K-loop is bound by
-// the rate at which the copies stream operands from L2/MALL into LDS.
+// Measured on MI355X (rocprofv3 counters): the K-loop is bound by the rate
+// at which each CU's vector L1 streams operands from L2 into LDS. A CU keeps
+// only some 40-70 L1->L2 requests in flight at ~300 cycles each, so per-CU
+// bandwidth is set by the bytes each request carries and by latency: a
+// 128-byte K-step turns every request into a whole L2 line, and it pays off
+// together with more copy-issuing waves (4 producers: +10-13% on the 192
+// tile). Deeper rings, an L2 prefetch copy and non-temporal output stores
+// were all slower.
 // Both operands are K-contiguous ("TN"). K % 64 == 0, N % 16 == 0.
 
 #include "common.h"
@@ -86,7 +92,10 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   constexpr int DW = NP > 0 ? NP : NW;          // waves that issue copies
   constexpr int LW = (BM + BN) / (RPI * DW);    // DMA instructions per copying wave per stage
   constexpr int H = BK / 32;                    // 32-k slices per K-step
-  static_assert(BK == 64, "K-step (the LDS swizzle assumes 4 chunks per row)");
+  static_assert(BK == 64 || BK == 128, "K-step");
+  // LDS bank swizzle: 16-byte chunk c of stage row r sits in slot c ^ swz(r),
+  // swz(r) = (r / RPB) % CPR with RPB = 256 / BK rows per 256-byte bank line
+  constexpr int RPB = 256 / BK;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * DW) == 0, "tile shape");
   static_assert((NS - 1) * LW < 64, "copies in flight per wave must fit vmcnt");
   static_assert(NS >= 3, "the K-loop waits for stage s+1 before issuing stage s+NS-1");
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int p = lane % CPR;
     is_w[t] = (RPI * q) < BN;  // whole instruction in one region (BN % RPI == 0)
     // LDS slot p of the row holds global chunk p ^ swz(row) (bank swizzle)
-    const uint32_t chunk = (uint32_t)(p ^ ((row >> 2) & 3));
+    const uint32_t chunk = (uint32_t)(p ^ ((row / RPB) % CPR));
     if (row < BN) {
       const int n = min(n0 + row, N - 1) - n0;
       voff[t] = (uint32_t)n * (uint32_t)K + 16u * chunk;
@@ -177,22 +186,35 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   auto wait_stage_runtime = [&](int p) {  // p = later stages allowed to stay pending
     if (p >= NS - 2) {
       wait_vmcnt<(NS - 2) * LW>();
-    } else if (p == 3) {
-      wait_vmcnt<3 * LW>();
-    } else if (p == 2) {
-      wait_vmcnt<2 * LW>();
-    } else if (p == 1) {
-      wait_vmcnt<LW>();
-    } else {
-      wait_vmcnt<0>();
+      return;
     }
+    if constexpr (NS - 2 > 3) {
+      if (p == 3) {
+        wait_vmcnt<(NS - 2 > 3 ? 3 * LW : 0)>();
+        return;
+      }
+    }
+    if constexpr (NS - 2 > 2) {
+      if (p == 2) {
+        wait_vmcnt<(NS - 2 > 2 ? 2 * LW : 0)>();
+        return;
+      }
+    }
+    if constexpr (NS - 2 > 1) {
+      if (p == 1) {
+        wait_vmcnt<(NS - 2 > 1 ? LW : 0)>();
+        return;
+      }
+    }
+    wait_vmcnt<0>();
   };
 
   if constexpr (NP > 0) {
     if (wave >= NW) {
       // ---- producer: stage s+1 landed before the barrier that ends step
       // s; after it, the slot of stage s-1 (read by every consumer before
-      // that barrier) takes stage s+NS-1. Same barrier count as a consumer.
+      // that barrier) takes stage s+NS-1. Same barrier count as a consumer
+      // (one before the loop, one per step).
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s)
         if (s < nk) issue(s, s);
@@ -203,6 +225,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
         lds_barrier();
         if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
       }
+      lds_barrier();  // the consumers' last-step barrier
       return;
     }
   } else {
@@ -215,14 +238,14 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // half lane/32 of the 32-byte k-slice h of the K-step
   const int fr = lane & 31;
   const int fh = lane >> 5;
-  // Row r of a stage keeps its 16-byte chunk c in slot c ^ swz(r), with
-  // swz(r) = (r >> 2) & 3: the 16 lanes that read 16 consecutive rows at one
-  // chunk then hit 16 distinct 4-bank groups (with plain 64-byte rows, rows
-  // r and r + 4 share banks). Row blocks start at multiples of 32, so
-  // swz(row) = (fr >> 2) & 3 for every fragment of this lane.
-  const int swz = (fr >> 2) & 3;
-  const int dsw0 = 16 * (fh ^ swz);        // chunk fh of slice 0
-  const int dsw1 = 16 * ((2 + fh) ^ swz);  // chunk 2 + fh of slice 1
+  // The 16 lanes that read 16 consecutive rows at one chunk hit 16 distinct
+  // 16-byte bank groups (without the swizzle, rows RPB apart share banks).
+  // Row blocks start at multiples of 32, so swz(row) = (fr / RPB) % CPR for
+  // every fragment of this lane; slice h reads chunk 2h + fh.
+  const int swz = (fr / RPB) % CPR;
+  int dsw[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) dsw[h] = 16 * ((2 * h + fh) ^ swz);
   int aoff[NI], boff[NJ];
 #pragma unroll
   for (int i = 0; i < NI; ++i) aoff[i] = (wn * WTN + i * 32 + fr) * BK;
@@ -238,7 +261,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   constexpr int NF = NI + NJ;
   v4i xa[NI], xb[NJ], ya[NI], yb[NJ];
   auto read_slice = [&](int s, int h, v4i (&fa)[NI], v4i (&fb)[NJ]) {
-    const uint8_t* base = lds + (s % NS) * STAGE + (h == 0 ? dsw0 : dsw1);
+    const uint8_t* base = lds + (s % NS) * STAGE + dsw[h];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[j] = *reinterpret_cast<const v4i*>(base + boff[j]);
 #pragma unroll
@@ -293,14 +316,17 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // of stage s+NS-1.
   for (int s = 0; s < nk; ++s) {
     early_slices(s);
-    if (s + 1 < nk) {
-      if constexpr (NP == 0) wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
-      lds_barrier();
-      if constexpr (NP == 0) {
-        if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
-      }
-      read_slice(s + 1, 0, xa, xb);
+    if constexpr (NP == 0) wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
+    lds_barrier();
+    if constexpr (NP == 0) {
+      if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
     }
+    // Every step takes the same path, the last one included (its reads of
+    // a stale ring slot land in X and are never used): with a branch around
+    // the barrier and these reads, the compiler's LDS-wait count for the Y
+    // slice below merges the two paths and then waits for the X reads just
+    // issued, stalling the MFMAs behind the LDS latency once per step.
+    read_slice(s + 1, 0, xa, xb);
     mfma_slice(ya, yb);  // H is even: the last slice sits in Y
     sched_slice();
   }
@@ -375,7 +401,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 // over 256 CUs times the work of one tile, with a small penalty for the
 // lower operand reuse of smaller tiles.
 TileCfg choose_tile(int64_t m, int64_t n) {
-  const TileCfg cands[] = {{256, 256, 4, 1}, {192, 192, 6, 1}, {128, 128, 4, 2}};
+  const TileCfg cands[] = {{256, 256, 4, 1}, {192, 192, 3, 1}, {128, 128, 4, 2}};
   const double eff[] = {1.0, 0.95, 0.8};
   TileCfg best = cands[0];
   double best_t = 1e300;
@@ -395,16 +421,30 @@ TileCfg choose_tile(int64_t m, int64_t n) {
 
 }  // namespace
 
+// One configuration per tile size. The 192 tile streams 128-byte K-steps
+// (whole L2 lines per request) when K allows, with four producer waves.
+static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
+                              const float* s_w, const uint16_t* bias, int M, int N, int K,
+                              uint16_t* y, int32_t* acc, hipStream_t st) {
+  switch (tile) {
+    case 256:
+      return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+    case 192:
+      if (K % 128 == 0)
+        return launch_cfg<192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
+                                                          st);
+      return launch_cfg<192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+    default:
+      return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+  }
+}
+
 hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                        const uint16_t* bias, int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int32_t* acc, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  const TileCfg t = choose_tile(m, n);
-  if (t.bm == 256)
-    return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
-  if (t.bm == 192)
-    return launch_cfg<192, 192, 64, 2, 2, 6, 1, 2>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
-  return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+  return launch_tile(choose_tile(m, n).bm, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc,
+                     st);
 }
 
 hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
@@ -412,15 +452,7 @@ hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq
                             int64_t k, uint16_t* y, int32_t* acc, int tile, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
   if (tile == 0) return launch_gemm(xq, s_x, wq, s_w, bias, m, n, k, y, acc, st);
-  const int M = (int)m, N = (int)n, Kk = (int)k;
-  switch (tile) {
-    case 256:
-      return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
-    case 192:
-      return launch_cfg<192, 192, 64, 2, 2, 6, 1, 2>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
-    default:
-      return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, Kk, y, acc, st);
-  }
+  return launch_tile(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
 }
 
 }  // namespace convrot

@@ -205,7 +205,8 @@ def test_edge_weights(g):
 
 @pytest.mark.parametrize("tile", [0, 128, 192, 256])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (2, 32, 128), (255, 16, 192), (257, 272, 320),
-                                   (33, 1040, 64), (512, 512, 4096), (400, 592, 384)])
+                                   (33, 1040, 64), (512, 512, 4096), (400, 592, 384),
+                                   (300, 400, 1152), (300, 400, 1088)])
 def test_gemm_shapes(m, n, k, tile):
     _announce(f"gemm shape {m}x{n}x{k} tile={tile}")
     rng = np.random.default_rng(m * 7 + n)

@@ -13,11 +13,11 @@
 //     gfx950 it sustains the full int8 rate, the 16x16x64 form about half)
 //     with the weight rows in the A operand, so each lane's accumulators
 //     come in runs of 4 consecutive output columns;
-//   * K-step BK = 64 bytes, or 128 for the 192 tile when K allows; an
-//     NS-deep ring of LDS stages filled by global_load_lds_dwordx4 (global
-//     -> LDS, no VGPRs); one barrier per K-step; the copies of step s+NS-1
-//     are issued right after it. With producer waves, only they issue
-//     copies and wait for them;
+//   * K-step BK = 128 bytes when K % 128 == 0, else 64; an NS-deep ring of
+//     LDS stages filled by global_load_lds_dwordx4 (global -> LDS, no
+//     VGPRs); one barrier per K-step, right after which the copies of a
+//     later stage are issued (NS = 2: into the stage just read). With
+//     producer waves, only they issue copies and wait for them;
 //   * LDS stage: rows of BK bytes, weights then activations; each copy
 //     instruction fills 1024 / BK rows; within a row the 16-byte chunks are
 //     XOR-swizzled by row (below), which makes the fragment reads free of
@@ -28,10 +28,10 @@
 // at which each CU's vector L1 streams operands from L2 into LDS. A CU keeps
 // only some 40-70 L1->L2 requests in flight at ~300 cycles each, so per-CU
 // bandwidth is set by the bytes each request carries and by latency: a
-// 128-byte K-step turns every request into a whole L2 line, and it pays off
-// together with more copy-issuing waves (4 producers: +10-13% on the 192
-// tile). Deeper rings, an L2 prefetch copy and non-temporal output stores
-// were all slower.
+// 128-byte K-step turns every request into a whole L2 line (+9-37% over 64
+// bytes, even with the ring cut to two stages; on the 192 tile only
+// together with four copy-issuing waves). Deeper rings, an L2 prefetch copy
+// and non-temporal output stores were all slower.
 // Both operands are K-contiguous ("TN"). K % 64 == 0, N % 16 == 0.
 
 #include "common.h"
@@ -62,6 +62,11 @@ __device__ __forceinline__ void dma16(const int8_t* sbase, uint32_t voff, uint32
                :
                : "v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt, expcnt left unconstrained)
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
 }
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
@@ -97,8 +102,13 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // swz(r) = (r / RPB) % CPR with RPB = 256 / BK rows per 256-byte bank line
   constexpr int RPB = 256 / BK;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * DW) == 0, "tile shape");
-  static_assert((NS - 1) * LW < 64, "copies in flight per wave must fit vmcnt");
-  static_assert(NS >= 3, "the K-loop waits for stage s+1 before issuing stage s+NS-1");
+  // Ring of NS stages. The copies of stage s+LA are issued after the barrier
+  // of step s: with NS >= 3 into the slot of stage s-1 (LA = NS-1); with
+  // NS == 2 into the slot of stage s itself (LA = 2), which every wave has
+  // then finished reading (each waits for its LDS reads before the barrier).
+  constexpr int LA = NS >= 3 ? NS - 1 : 2;
+  static_assert(NS >= 2, "ring depth");
+  static_assert(LA * LW < 64, "copies in flight per wave must fit vmcnt");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -184,25 +194,25 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // a stage's copies are complete when at most the copies of the p later
   // stages are outstanding (copies complete in order)
   auto wait_stage_runtime = [&](int p) {  // p = later stages allowed to stay pending
-    if (p >= NS - 2) {
-      wait_vmcnt<(NS - 2) * LW>();
+    if (p >= LA - 1) {
+      wait_vmcnt<(LA - 1) * LW>();
       return;
     }
-    if constexpr (NS - 2 > 3) {
+    if constexpr (LA - 1 > 3) {
       if (p == 3) {
-        wait_vmcnt<(NS - 2 > 3 ? 3 * LW : 0)>();
+        wait_vmcnt<(LA - 1 > 3 ? 3 * LW : 0)>();
         return;
       }
     }
-    if constexpr (NS - 2 > 2) {
+    if constexpr (LA - 1 > 2) {
       if (p == 2) {
-        wait_vmcnt<(NS - 2 > 2 ? 2 * LW : 0)>();
+        wait_vmcnt<(LA - 1 > 2 ? 2 * LW : 0)>();
         return;
       }
     }
-    if constexpr (NS - 2 > 1) {
+    if constexpr (LA - 1 > 1) {
       if (p == 1) {
-        wait_vmcnt<(NS - 2 > 1 ? LW : 0)>();
+        wait_vmcnt<(LA - 1 > 1 ? LW : 0)>();
         return;
       }
     }
@@ -216,22 +226,22 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
       // that barrier) takes stage s+NS-1. Same barrier count as a consumer
       // (one before the loop, one per step).
 #pragma unroll
-      for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) issue(s, s);
-      wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
+      for (int s = 0; s < LA; ++s)
+        if (s < nk) issue(s, s % NS);
+      wait_stage_runtime(min(LA - 1, nk - 1));  // stage 0 landed
       lds_barrier();
       for (int s = 0; s + 1 < nk; ++s) {
-        wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
+        wait_stage_runtime(min(LA - 2, nk - 2 - s));  // stage s+1 landed
         lds_barrier();
-        if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
+        if (s + LA < nk) issue(s + LA, (s + LA) % NS);
       }
       lds_barrier();  // the consumers' last-step barrier
       return;
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < nk) issue(s, s);
+    for (int s = 0; s < LA; ++s)
+      if (s < nk) issue(s, s % NS);
   }
 
   // 32x32x32 operands: lane -> row lane%32 of a 32-row block, 16-byte
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // entry (they return out of order) makes every LDS-read wait in the loop
   // a full lgkmcnt(0) drain.
   asm volatile("" ::"s"(y), "s"(acc_out), "s"(s_x), "s"(s_w), "s"(bias));
-  if constexpr (NP == 0) wait_stage_runtime(min(NS - 2, nk - 1));  // stage 0 landed
+  if constexpr (NP == 0) wait_stage_runtime(min(LA - 1, nk - 1));  // stage 0 landed
   lds_barrier();
   read_slice(0, 0, xa, xb);
   // One uniform loop (no separate tail copy, which would double the live
@@ -316,10 +326,11 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // of stage s+NS-1.
   for (int s = 0; s < nk; ++s) {
     early_slices(s);
-    if constexpr (NP == 0) wait_stage_runtime(min(NS - 3, nk - 2 - s));  // stage s+1 landed
+    if constexpr (NP == 0) wait_stage_runtime(min(LA - 2, nk - 2 - s));  // stage s+1 landed
+    if constexpr (NS == 2) wait_lgkm0();  // this wave's reads of stage s are done
     lds_barrier();
     if constexpr (NP == 0) {
-      if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
+      if (s + LA < nk) issue(s + LA, (s + LA) % NS);
     }
     // Every step takes the same path, the last one included (its reads of
     // a stale ring slot land in X and are never used): with a branch around
@@ -401,8 +412,9 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 // over 256 CUs times the work of one tile, with a small penalty for the
 // lower operand reuse of smaller tiles.
 TileCfg choose_tile(int64_t m, int64_t n) {
-  const TileCfg cands[] = {{256, 256, 4, 1}, {192, 192, 3, 1}, {128, 128, 4, 2}};
-  const double eff[] = {1.0, 0.95, 0.8};
+  const TileCfg cands[] = {{256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
+  // relative throughput per tile round (measured on full rounds)
+  const double eff[] = {1.0, 0.8, 0.8};
   TileCfg best = cands[0];
   double best_t = 1e300;
   for (int c = 0; c < 3; ++c) {
@@ -421,13 +433,17 @@ TileCfg choose_tile(int64_t m, int64_t n) {
 
 }  // namespace
 
-// One configuration per tile size. The 192 tile streams 128-byte K-steps
-// (whole L2 lines per request) when K allows, with four producer waves.
+// One configuration per tile size. When K allows, every tile streams
+// 128-byte K-steps (whole L2 lines per request): a two-stage ring for the
+// 256 and 128 tiles (64 and 32 KB stages), three stages and four producer
+// waves for the 192 tile. Otherwise 64-byte K-steps with deeper rings.
 static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
                               const float* s_w, const uint16_t* bias, int M, int N, int K,
                               uint16_t* y, int32_t* acc, hipStream_t st) {
   switch (tile) {
     case 256:
+      if (K % 128 == 0)
+        return launch_cfg<256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
       return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     case 192:
       if (K % 128 == 0)
@@ -435,6 +451,8 @@ static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, cons
                                                           st);
       return launch_cfg<192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     default:
+      if (K % 128 == 0)
+        return launch_cfg<128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
       return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
   }
 }

@@ -74,11 +74,24 @@ def _traffic(n_launch_units: float):
 
 
 def _events_time(fn, reps, stream):
-    """Per-launch GPU duration from HIP events recorded on `stream` around each
-    call. The stream is first held by a GPU sleep long enough for the host to
-    enqueue every call, so the events bracket the kernels alone, not host
-    launch gaps. Returns (mean, min, median) in ms."""
+    """GPU duration per launch from HIP events recorded on `stream`. The stream
+    is first held by a GPU sleep long enough for the host to enqueue every
+    call, so the events bracket the kernels alone, not host launch gaps.
+    Returns (mean, min, median) in ms: the mean over one batch of `reps`
+    back-to-back launches between two events (per-event overhead amortised,
+    as a kernel trace sees it), min and median over launches bracketed one by
+    one."""
     import torch
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(reps):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    mean = t0.elapsed_time(t1) / reps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     with torch.cuda.stream(stream):
@@ -89,7 +102,7 @@ def _events_time(fn, reps, stream):
         ends[i].record(stream)
     torch.cuda.synchronize()
     ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return sum(ms) / len(ms), ms[0], ms[len(ms) // 2]
+    return mean, ms[0], ms[len(ms) // 2]
 
 
 def _cpu_baseline(layer, g, seed, target_s):

@@ -12,6 +12,14 @@
 //     53 bits and float64 is exact. Rows holding a group outside that bound
 //     (or rows too small for the folded scaling below) are left to the exact
 //     kernel: their scale slot receives the kDeferredRow NaN.
+//   * Deferred rows (the exact kernel's deferred mode) first get one rounded
+//     float64 transform: each output is within log2(g) * 2^-53 * sum|x| of
+//     the exact sum (a depth-log2(g) tree of rounded additions), so with
+//     that bound (and margin) an element either provably rounds to
+//     RN32(y), or to one of RN32(y) and its neighbour. The row is finished
+//     there unless such an undecided element could be the row's absmax or
+//     quantizes differently for its two candidates (ties decided only by
+//     elements the float64 sum lost: GELU-tailed activations).
 //   * Exact kernel: splits each group's elements into bands of kBand
 //     binades (each band's transform is exact in float64), turns each band's
 //     sums into integers of the band's quantum and adds the bands bottom-up
@@ -57,6 +65,25 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kQuadRev = 0x1B;   // quad_perm [3,2,1,0]: lane i <- i ^ 3
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <- 7 - i within 8 lanes
+
+// lane i <- lane i ^ M (M = 1, 2, 4) with DPP moves; xor 4 is the half-row
+// mirror (i ^ 7) followed by the quad reversal (i ^ 3)
+template <int M>
+__device__ __forceinline__ uint32_t xor_lanes_u32(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4, "lane xor");
+  if constexpr (M == 1) return dpp_u32<kQuadXor1>(v);
+  if constexpr (M == 2) return dpp_u32<kQuadXor2>(v);
+  return dpp_u32<kQuadRev>(dpp_u32<kHalfMirror>(v));
+}
+template <int M>
+__device__ __forceinline__ double xor_lanes_f64(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = xor_lanes_u32<M>((uint32_t)b);
+  const uint32_t hi = xor_lanes_u32<M>((uint32_t)(b >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
   const uint64_t b = __double_as_longlong(v);
@@ -312,7 +339,7 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
 
 enum ExactMode : int { kRowAll = 0, kRowDeferred = 1, kTensorMax = 2, kTensorQuant = 3 };
 
-template <int G>
+template <int G, bool WIDE>
 __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
     uint32_t* __restrict__ tensor_amax, int64_t rows, int K, int T, int rows_per_block,
@@ -325,6 +352,8 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   constexpr int LPG = G >= CH ? G / CH : 1;  // lanes per group
   __shared__ uint32_t s_rowmax[256];
   __shared__ uint32_t s_rowflag[256];
+  __shared__ uint32_t s_rowunc[256];   // 1 + bits of an undecided element's larger candidate
+  __shared__ uint32_t s_rowconf[256];  // an undecided element quantizes both ways
 
   const int tid = threadIdx.x;
   const int r_in = tid / T;
@@ -351,6 +380,8 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   if (tid < rows_per_block) {
     s_rowmax[tid] = 0u;
     s_rowflag[tid] = 0u;
+    s_rowunc[tid] = 0u;
+    s_rowconf[tid] = 0u;
   }
   if (mode == kRowDeferred) {
     // rows that the fast kernel finished are skipped as a whole
@@ -377,6 +408,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   // per group: largest exponent field E and band count
   int egrp[NGL];
   int nb_lane = 0;
+  uint32_t gmask = 0u;  // bit gidx: group gidx spans more than float64 adds exactly
 #pragma unroll
   for (int gidx = 0; gidx < NGL; ++gidx) {
     us2 mx = (us2)(0), mn = (us2)(0xFFFF);
@@ -391,6 +423,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
       b = b < tb ? b : tb;
     }
     const int span = group_span(a, b);
+    if (span > 45 - LOGG) gmask |= 1u << gidx;
     int e = (int)(a >> 7);
     egrp[gidx] = e < 1 ? 1 : e;
     const int nb = span < 0 ? 0 : span / kBand + 1;
@@ -402,6 +435,129 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   for (int m = 1; m < 64; m <<= 1) {
     const int t = __shfl_xor(nb_all, m);
     nb_all = nb_all > t ? nb_all : t;
+  }
+
+  if constexpr (WIDE) {
+    // ---- one rounded float64 transform first (rows the fast kernel left:
+    // mostly wide-span groups). Each output is a depth-LOGG tree of correctly
+    // rounded additions, so it is within LOGG * 2^-53 * S of the exact sum
+    // (S = sum |x| over the group); delta = 2^-46 * S' bounds that with a wide
+    // margin (S' = fp32 sum of |x| over the group for g >= 32, over the lane
+    // otherwise). With u = RN32(y) and d = y - u (exact), the exact sum rounds
+    // to u when |d| + delta is below the half-gap h from u to its next
+    // rounding boundary (ulp/2, ulp/4 at a power of two, 2^-151 at zero);
+    // h is a power of two, so the float64 test is exact. Otherwise, with
+    // delta < h, it rounds to u or to u's neighbour on the side of y
+    // (undecided). The row is finished here unless an undecided element
+    // could be its absmax or quantizes differently for its two candidates.
+    float u[CH];
+    uint64_t umask = 0ull, dmask = 0ull;
+    uint32_t unc_hi = 0u;
+    bool unsafe = false;
+    float wamax = 0.0f;
+    {
+      double y[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        y[i] = (double)__uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+      float sabs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) sabs += fabsf((float)y[i]);
+      fwht_inlane<G, CH>(y);
+      // cross-lane stages over the LPG lanes of a group (DPP, in-row)
+      auto xstage = [&](auto mt) {
+        constexpr int m = decltype(mt)::value;
+        const double sg = ((c & m) != 0) ? -1.0 : 1.0;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) y[i] = __builtin_fma(y[i], sg, xor_lanes_f64<m>(y[i]));
+        sabs += __uint_as_float(xor_lanes_u32<m>(__float_as_uint(sabs)));
+      };
+      if constexpr (LPG > 1) xstage(std::integral_constant<int, 1>{});
+      if constexpr (LPG > 2) xstage(std::integral_constant<int, 2>{});
+      if constexpr (LPG > 4) xstage(std::integral_constant<int, 4>{});
+      static_assert(LPG <= 8, "group spans at most 8 lanes");
+      const double delta = (double)sabs * 0x1p-46;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        u[i] = (float)y[i];
+        wamax = fmaxf(wamax, fabsf(u[i]));
+        const uint32_t rb = __float_as_uint(u[i]);
+        uint32_t ef = (rb >> 23) & 0xFFu;
+        ef = ef < 1u ? 1u : ef;
+        const uint32_t pow2 = (rb & 0x7FFFFFu) == 0u ? 1u : 0u;
+        const double h =
+            __longlong_as_double((int64_t)(uint64_t)(ef + (1023u - 151u) - pow2) << 52);
+        const double d = y[i] - (double)u[i];
+        const bool wide = (gmask >> (i / GE)) & 1u;
+        const bool und = wide && !(fabs(d) + delta < h);
+        unsafe |= und && !(delta < h);
+        const uint32_t mb = rb & 0x7FFFFFFFu;
+        const bool away = (d > 0.0) == !(rb >> 31) || mb == 0u;
+        umask |= (uint64_t)und << i;
+        dmask |= (uint64_t)(und && away) << i;
+        const uint32_t hb = und ? mb + (away ? 1u : 0u) : 0u;
+        unc_hi = hb > unc_hi ? hb : unc_hi;
+      }
+    }
+    if (active) {
+      atomicMax(&s_rowmax[r_in], __float_as_uint(wamax));
+      if (unsafe) atomicOr(&s_rowflag[r_in], 1u);
+      if (umask != 0ull) atomicMax(&s_rowunc[r_in], unc_hi + 1u);
+    }
+    __syncthreads();
+    const float amax_u = __uint_as_float(s_rowmax[r_in]);
+    const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact when not deferred
+    const uint32_t rowunc = s_rowunc[r_in];
+    bool wide_ok = active && s_rowflag[r_in] == 0u && amax_u <= 3.0e38f &&
+                   !(amax_u > 0.0f && amax_x < 0x1p-100f) &&
+                   !(rowunc != 0u && rowunc - 1u >= __float_as_uint(amax_u));
+    float wsc = 0.0f;
+    uint32_t wout[CH / 4];
+    if (wide_ok) {
+      float inv_u = 0.0f;
+      if (amax_u > 0.0f) {
+        wsc = amax_x / 127.0f;
+        inv_u = (127.0f / amax_x) * (1.0f / (float)(1 << KS));
+      }
+      const int base_j = (G >= CH) ? CH * (c % LPG) : 0;
+      bool conflict = false;
+#pragma unroll
+      for (int d4 = 0; d4 < CH / 4; ++d4) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * d4 + e;
+          const int j = (G >= CH) ? base_j + i : (i % G);
+          const float sgn = sign_bit(sm, j) ? -1.0f : 1.0f;
+          b[e] = __float_as_uint((sgn * u[i]) * inv_u + kQuantPlain);
+          // the other candidate of an undecided element (u's sign; a zero's
+          // sign does not reach q)
+          const uint32_t rb = __float_as_uint(u[i]);
+          const uint32_t mb = rb & 0x7FFFFFFFu;
+          const uint32_t nb = ((dmask >> i) & 1ull) ? mb + 1u : mb - 1u;
+          const float un = __uint_as_float((rb & 0x80000000u) | nb);
+          const uint32_t b2 = __float_as_uint((sgn * un) * inv_u + kQuantPlain);
+          conflict |= ((umask >> i) & 1ull) && ((b[e] ^ b2) & 0xFFu) != 0u;
+        }
+        const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+        const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+        wout[d4] = t0 | t1;
+      }
+      if (conflict) atomicOr(&s_rowconf[r_in], 1u);
+    }
+    __syncthreads();  // conflicts published; s_rowmax readers done
+    wide_ok = wide_ok && s_rowconf[r_in] == 0u;
+    if (wide_ok) {
+      uint4* o = reinterpret_cast<uint4*>(xq + row * (int64_t)K + (int64_t)CH * c);
+#pragma unroll
+      for (int i = 0; i < CH / 16; ++i)
+        o[i] = make_uint4(wout[4 * i], wout[4 * i + 1], wout[4 * i + 2], wout[4 * i + 3]);
+      if (c == 0) scale[row] = wsc;
+    }
+    // the banded algorithm below for the rows still open
+    active = active && !wide_ok;
+    if (tid < rows_per_block) s_rowmax[tid] = 0u;  // published by the barrier below
+    if (__syncthreads_or(active) == 0) continue;
   }
 
   double V[CH];
@@ -584,8 +740,11 @@ hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tenso
   int64_t cap = (int64_t)kNumCUs * wpc / (ts.block / 64);
   if (cap < 1) cap = 1;
   const int64_t blocks = nbatches < cap ? nbatches : cap;
-  hipLaunchKernelGGL(rotate_quant_exact_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0,
-                     st, x, xq, s, tensor_amax, rows, K, ts.T, ts.rpb, nbatches, sm, mode);
+  // rows the fast kernel left get a rounded float64 transform first
+  auto kern = mode == kRowDeferred ? rotate_quant_exact_kernel<G, true>
+                                   : rotate_quant_exact_kernel<G, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ts.block), 0, st, x, xq, s, tensor_amax,
+                     rows, K, ts.T, ts.rpb, nbatches, sm, mode);
   return hipGetLastError();
 }
 

@@ -174,6 +174,17 @@ def _edge_rows(k):
     r = rng.standard_normal(k); r[::7] = 1e-38; rows.append(r)  # tiny normals beside O(1)
     rows.append(rng.standard_normal(k) * 1e30)                 # large
     rows.append(np.where(rng.random(k) < 0.5, 1.0, -1.0) * 2.0 ** rng.integers(-20, 20, k))
+    # fp32 ties decided only by a tiny element: in every other 256-block a
+    # group holds 1, 2^-24 and +-2^-100, so the float64 transform lands exactly
+    # on an fp32 midpoint that the lost 2^-100 term breaks; the other blocks
+    # hold 100.0 (the row absmax) or nothing (the tie group holds the absmax)
+    for tiny, big in ((2.0 ** -100, 100.0), (-(2.0 ** -100), 100.0), (2.0 ** -100, 0.0)):
+        r = np.zeros(k)
+        for s0 in range(0, k, 512):
+            r[s0], r[s0 + 1], r[s0 + 2] = 1.0, 2.0 ** -24, tiny
+            if s0 + 256 < k:
+                r[s0 + 256] = big
+        rows.append(r)
     return synth.f32_to_bf16_bits(np.array(rows, dtype=np.float32))
 
 

@@ -212,6 +212,29 @@ def main():
         lambda i: cr.convrot_dequant_derotate(wqs[i % nrot_w], s_w, g, seed,
                                               out=outs[i % nrot_w]), reps, stream)
     torch.cuda.synchronize()
+    del wqs, outs
+
+    # ---- dequant over the 60-layer stack: 60 + 60 distinct int8 buffers of
+    # the two stack shapes, one dequant each per pass, outputs rotated over 4 ----
+    stack = []
+    for lay in (synth.STACK_SQUARE, synth.STACK_WIDE):
+        wq_l, sw_l = cr.convrot_quantize_weights(to_dev(lay.w()), g, seed)
+        copies = [wq_l.clone() for _ in range(synth.STACK_LAYERS)]
+        del wq_l
+        outs_l = [torch.empty((lay.n, lay.k), dtype=torch.bfloat16, device=dev)
+                  for _ in range(4)]
+        stack.append((copies, sw_l, outs_l))
+
+    def stack_pass(i):
+        for layer_i in range(synth.STACK_LAYERS):
+            for copies, sw_l, outs_l in stack:
+                cr.convrot_dequant_derotate(copies[layer_i], sw_l, g, seed,
+                                            out=outs_l[layer_i % 4])
+
+    stack_ms, stack_min, _ = _events_time(stack_pass, 3, stream)
+    stack_bytes = float(sum(3 * c[0].numel() * len(c) + 4 * len(c) for c, _, _ in stack))
+    del stack
+    torch.cuda.synchronize()
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -258,6 +281,10 @@ def main():
         "dequant": {"GB/s": round(deq_gbs, 1), "frac_hbm": round(deq_gbs / PEAK_HBM_GBS, 4),
                     "avg_ms": round(deq_ms, 5), "min_ms": round(deq_min, 5),
                     "bytes": deq_bytes, "buffers_rotated": nrot_w},
+        "dequant_stack": {"layers": 2 * synth.STACK_LAYERS,
+                          "GB/s": round(stack_bytes / (stack_ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(stack_bytes / (stack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "ms_per_pass": round(stack_ms, 4), "bytes": stack_bytes},
         "linear_tops_frac_peak": round(value / PEAK_INT8_TOPS, 4),
     }
     if not args.no_cpu_baseline:

@@ -116,3 +116,22 @@ def test_fullsize(layer, g):
     # and the epilogue of the same launch on those columns
     y_cols = oracle.epilogue(got.astype(np.int64), s_ref, s_x.cpu().numpy())
     assert np.array_equal(host_bits(y2[:, cols_t].contiguous()), y_cols)
+
+
+def test_dequant_stack_layers_0_and_59():
+    """The streamed stack: each stack weight quantized once and copied into 60
+    distinct device buffers; layers 0 and 59 dequantize bit-exactly (the same
+    launch the benchmark's stack pass makes, per buffer)."""
+    g = 256
+    for lay in (synth.STACK_SQUARE, synth.STACK_WIDE):
+        print(f"dequant stack {lay.name}", flush=True)
+        wb = lay.w()
+        wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
+        wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+        assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
+        copies = [wq.clone() for _ in range(synth.STACK_LAYERS)]
+        want = oracle.dequant_derotate(wq_ref, s_ref, g, SEED)
+        for li in (0, synth.STACK_LAYERS - 1):
+            out = cr.convrot_dequant_derotate(copies[li], s_w, g, SEED)
+            assert np.array_equal(host_bits(out), want), li
+        del copies

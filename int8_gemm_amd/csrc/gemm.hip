@@ -15,9 +15,10 @@
 //     come in runs of 4 consecutive output columns;
 //   * K-step BK = 128 bytes when K % 128 == 0, else 64; an NS-deep ring of
 //     LDS stages filled by global_load_lds_dwordx4 (global -> LDS, no
-//     VGPRs); one barrier per K-step, right after which the copies of a
-//     later stage are issued (NS = 2: into the stage just read). With
-//     producer waves, only they issue copies and wait for them;
+//     VGPRs); one barrier per K-step, right after which the copies of stage
+//     s+NS go into the slot of the stage s just read (every wave waits for
+//     its LDS reads before the barrier). With producer waves, only they
+//     issue copies and wait for them;
 //   * LDS stage: rows of BK bytes, weights then activations; each copy
 //     instruction fills 1024 / BK rows; within a row the 16-byte chunks are
 //     XOR-swizzled by row (below), which makes the fragment reads free of
@@ -102,11 +103,11 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // swz(r) = (r / RPB) % CPR with RPB = 256 / BK rows per 256-byte bank line
   constexpr int RPB = 256 / BK;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (BM + BN) % (RPI * DW) == 0, "tile shape");
-  // Ring of NS stages. The copies of stage s+LA are issued after the barrier
-  // of step s: with NS >= 3 into the slot of stage s-1 (LA = NS-1); with
-  // NS == 2 into the slot of stage s itself (LA = 2), which every wave has
-  // then finished reading (each waits for its LDS reads before the barrier).
-  constexpr int LA = NS >= 3 ? NS - 1 : 2;
+  // Ring of NS stages. Every consumer wave waits for its own LDS reads before
+  // the barrier of step s, so after it nobody reads stage s again (its last
+  // slice is in registers): the copies of stage s+NS go into stage s's slot
+  // right after that barrier, and NS-1 stages stay in flight during a step.
+  constexpr int LA = NS;
   static_assert(NS >= 2, "ring depth");
   static_assert(LA * LW < 64, "copies in flight per wave must fit vmcnt");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   for (int s = 0; s < nk; ++s) {
     early_slices(s);
     if constexpr (NP == 0) wait_stage_runtime(min(LA - 2, nk - 2 - s));  // stage s+1 landed
-    if constexpr (NS == 2) wait_lgkm0();  // this wave's reads of stage s are done
+    wait_lgkm0();  // this wave's reads of stage s are done before the barrier
     lds_barrier();
     if constexpr (NP == 0) {
       if (s + LA < nk) issue(s + LA, (s + LA) % NS);
@@ -414,7 +415,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 TileCfg choose_tile(int64_t m, int64_t n) {
   const TileCfg cands[] = {{256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
   // relative throughput per tile round (measured on full rounds)
-  const double eff[] = {1.0, 0.8, 0.8};
+  const double eff[] = {1.0, 0.9, 0.8};
   TileCfg best = cands[0];
   double best_t = 1e300;
   for (int c = 0; c < 3; ++c) {

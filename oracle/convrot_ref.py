@@ -33,6 +33,13 @@ What the pages leave open, and the reading taken here
   with S = (Wq . D) . H per group in exact integers.
 * GEMM epilogue: y = RN_bf16(RN_fp32(RN_fp32(float(acc) * s_w) * s_x[m])
   (+ bias[n], added in fp32)).
+* Per-output-channel scales (the next step the pages point to: published int8
+  convrot checkpoints carry one fp32 scale per output channel, and any weight
+  scale multiplies output rows -- PR "share the int8_convrot scheme ... Krea-2
+  and Z-Image", "Z-Image: the fused QKV" and the scale-layout fix in its
+  commit list): s_w[n] = RN(amax_n/127) over row n of the rotated weight,
+  the row quantized with it as a token row is; dequant uses RN(s_w[n]*2^-k)
+  for row n; the epilogue uses s_w[n] for output column n.
 
 Arithmetic is float64 (exact where the text says so) or exact integers.
 """
@@ -274,6 +281,26 @@ def quantize_weights(w_bits: np.ndarray, g: int, seed: int):
     return q, np.float32(s[0] if s.size else 0.0)
 
 
+def quantize_weights_per_channel(w_bits: np.ndarray, g: int, seed: int):
+    """Per-output-channel rotate + absmax + int8 quantize of W [N, K]: row n of
+    the rotated weight gets s_w[n] = RN(amax_n/127) and is quantized with it.
+    Returns Wq int8 [N, K], s_w float32 [N]."""
+    wr = rotate_rows(w_bits, g, seed)
+    amax = np.abs(wr).max(axis=1) if wr.shape[1] else np.zeros(wr.shape[0], np.float32)
+    return quantize_with_amax(wr, amax.astype(np.float32))
+
+
+def _row_scales(s_w, n: int) -> np.ndarray:
+    """s_w as float32 [n]: a per-tensor scale repeated, or the per-channel
+    vector itself (one scale per output row)."""
+    sw = np.asarray(s_w, dtype=np.float32)
+    if sw.ndim == 0:
+        return np.full(n, sw, dtype=np.float32)
+    if sw.shape != (n,):
+        raise ValueError("a per-channel scale has one entry per output row")
+    return sw
+
+
 # ----------------------------------------------------------------------------
 # Dequant + derotate (default path)
 # ----------------------------------------------------------------------------
@@ -288,19 +315,22 @@ def derotation_integers(wq: np.ndarray, g: int, seed: int) -> np.ndarray:
 
 
 def dequant_derotate(wq: np.ndarray, s_w, g: int, seed: int) -> np.ndarray:
-    """W_hat (bf16 bits) = RN_bf16(RN32(float(S) * c)), c = RN32(s_w*2^-k)."""
+    """W_hat (bf16 bits) = RN_bf16(RN32(float(S) * c)), c = RN32(s_w*2^-k);
+    with a per-channel s_w [N], row n uses c_n = RN32(s_w[n]*2^-k)."""
     k = int(math.log2(math.isqrt(g)))
-    c = np.float32(np.float32(s_w) * np.float32(2.0 ** -k))
+    c = (_row_scales(s_w, wq.shape[0]) * np.float32(2.0 ** -k)).astype(np.float32)
     s_int = derotation_integers(wq, g, seed)
-    return f32_to_bf16((s_int.astype(np.float32) * c).astype(np.float32))
+    return f32_to_bf16((s_int.astype(np.float32) * c[:, None]).astype(np.float32))
 
 
 def dequant_reference_f64(wq: np.ndarray, s_w, g: int, seed: int) -> np.ndarray:
-    """s_w * Wq . blockdiag(R)^T in float64 (the tolerance reference)."""
+    """s_w * Wq . blockdiag(R)^T in float64 (the tolerance reference); a
+    per-channel s_w scales the rows."""
     r = rotation_matrix(g, seed)
     n, kdim = wq.shape
     grp = wq.reshape(-1, g).astype(np.float64)
-    return (float(s_w) * (grp @ r.T)).reshape(n, kdim)
+    sw = _row_scales(s_w, n).astype(np.float64)
+    return sw[:, None] * (grp @ r.T).reshape(n, kdim)
 
 
 # ----------------------------------------------------------------------------
@@ -319,9 +349,10 @@ def gemm_int32(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
 
 
 def epilogue(acc: np.ndarray, s_w, s_x: np.ndarray, bias_bits: np.ndarray | None = None):
-    """y = RN_bf16(RN32(RN32(float(acc) * s_w) * s_x[m]) [+ bias[n]]) -> bf16 bits."""
+    """y = RN_bf16(RN32(RN32(float(acc) * s_w) * s_x[m]) [+ bias[n]]) -> bf16 bits;
+    a per-channel s_w [N] scales output column n."""
     t = acc.astype(np.float32)
-    t = (t * np.float32(s_w)).astype(np.float32)
+    t = (t * _row_scales(s_w, acc.shape[1])[None, :]).astype(np.float32)
     t = (t * np.asarray(s_x, dtype=np.float32)[:, None]).astype(np.float32)
     if bias_bits is not None:
         t = (t + bf16_to_f64(bias_bits).astype(np.float32)[None, :]).astype(np.float32)
@@ -341,7 +372,8 @@ def linear_int8_reference_f64(acc: np.ndarray, s_w, s_x: np.ndarray,
                               bias_bits: np.ndarray | None = None) -> np.ndarray:
     """s_w * s_x[m] * acc (+ bias) in float64: the tolerance reference of the
     int8_compute output."""
-    y = float(s_w) * np.asarray(s_x, dtype=np.float64)[:, None] * acc.astype(np.float64)
+    sw = _row_scales(s_w, acc.shape[1]).astype(np.float64)
+    y = sw[None, :] * np.asarray(s_x, dtype=np.float64)[:, None] * acc.astype(np.float64)
     if bias_bits is not None:
         y = y + bf16_to_f64(bias_bits)[None, :]
     return y

@@ -398,3 +398,119 @@ def test_linear_int8_tiny_tolerances():
     assert o.rel_frobenius(yb, true) < 0.05
     deq = o.dequant_linear_reference_f64(xb, wq, s_w, 256, SEED)
     assert o.rel_frobenius(deq, true) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Per-output-channel weight scales: one fp32 scale per row of W, i.e. per
+# output column of y (PR "share the int8_convrot scheme ... Krea-2 and
+# Z-Image", "Z-Image: the fused QKV"; the scale-layout fix in its commits)
+# --------------------------------------------------------------------------
+
+def _rowscaled_weight(n, k, rng):
+    """bf16 weight whose row magnitudes span 2^-12 .. 2^12"""
+    w = rng.standard_normal((n, k)) * 0.02
+    w *= 2.0 ** rng.integers(-12, 13, n)[:, None]
+    return synth.f32_to_bf16_bits(w.astype(np.float32))
+
+
+@pytest.mark.parametrize("g", GS)
+def test_per_channel_quantize_is_per_tensor_of_each_row(g):
+    rng = np.random.default_rng(30 + g)
+    wb = _rowscaled_weight(12, 512, rng)
+    wq, s = o.quantize_weights_per_channel(wb, g, SEED)
+    assert s.shape == (12,) and s.dtype == np.float32 and wq.dtype == np.int8
+    for n in range(12):
+        q1, s1 = o.quantize_weights(wb[n:n + 1], g, SEED)
+        assert np.array_equal(wq[n], q1[0]) and s[n] == s1
+        assert np.abs(wq[n].astype(np.int64)).max() == 127
+
+
+def test_per_channel_power_of_two_row_scaling():
+    """rows 2^e * v quantize to the same codes with scales 2^e * s; one
+    per-tensor scale flushes the small rows to zero"""
+    rng = np.random.default_rng(31)
+    v = o.bf16_to_f64(synth.f32_to_bf16_bits((rng.standard_normal((1, 256)) * 0.05)
+                                             .astype(np.float32)))
+    e = np.arange(-10, 11, 4)
+    wb = synth.f32_to_bf16_bits((v * 2.0 ** e[:, None]).astype(np.float32))
+    for g in GS:
+        wq, s = o.quantize_weights_per_channel(wb, g, SEED)
+        assert (wq == wq[0]).all()
+        assert np.array_equal(s.astype(np.float64), float(s[0]) * 2.0 ** (e - e[0]))
+        wq_t, _ = o.quantize_weights(wb, g, SEED)
+        assert not wq_t[0].any() and np.array_equal(wq_t[-1], wq[-1])
+
+
+@pytest.mark.parametrize("g", (16, 64))
+def test_per_channel_dequant_recovers_row_impulses_on_square_weight(g):
+    """Square W (out == in), row n one impulse of its own magnitude: the
+    per-channel decode returns W exactly. Applying the scales along the input
+    axis instead (the broadcast the pages' fix removed) would not."""
+    k = 64
+    w = np.zeros((k, k), dtype=np.float32)
+    for n in range(k):
+        w[n, (7 * n) % k] = (-1.0) ** n * 2.0 ** ((n % 13) - 6)
+    wq, s = o.quantize_weights_per_channel(synth.f32_to_bf16_bits(w), g, SEED)
+    w_hat = o.bf16_to_f64(o.dequant_derotate(wq, s, g, SEED))
+    assert np.array_equal(w_hat, w.astype(np.float64))
+    ref = o.dequant_reference_f64(wq, s, g, SEED)
+    # float64 decode: off only by the fp32 rounding of each row's scale
+    assert (np.abs(ref - w).max(axis=1) <= 2.0 ** -23 * np.abs(w).max(axis=1)).all()
+    # the wrong broadcast (scales over input columns) misdecodes most rows
+    k_ = int(math.log2(math.isqrt(g)))
+    s_int = o.derotation_integers(wq, g, SEED).astype(np.float64)
+    wrong = s_int * (s.astype(np.float64) * 2.0 ** -k_)[None, :]
+    assert (np.abs(wrong - w).max(axis=1) > 0.5 * np.abs(w).max(axis=1)).sum() > k // 2
+
+
+def test_per_channel_dequant_constant_scales_is_per_tensor():
+    rng = np.random.default_rng(33)
+    wq = rng.integers(-127, 128, (8, 512)).astype(np.int8)
+    for g in GS:
+        sw = np.float32(0.0123)
+        assert np.array_equal(o.dequant_derotate(wq, np.full(8, sw, np.float32), g, SEED),
+                              o.dequant_derotate(wq, sw, g, SEED))
+
+
+def test_per_channel_epilogue_closed_form():
+    """acc = 1 everywhere, s_x[m] = 2^m, s_w[n] = 2^-n: y[m, n] = 2^(m - n)
+    (a scale applied along the wrong axis gives 2^(n - m) or 2^0)"""
+    m = n = 6
+    acc = np.ones((m, n), dtype=np.int32)
+    s_x = (2.0 ** np.arange(m)).astype(np.float32)
+    s_w = (2.0 ** -np.arange(n)).astype(np.float32)
+    y = o.bf16_to_f64(o.epilogue(acc, s_w, s_x))
+    assert np.array_equal(y, 2.0 ** (np.arange(m)[:, None] - np.arange(n)[None, :]))
+    # each column is the per-tensor epilogue with that column's scale
+    rng = np.random.default_rng(34)
+    acc = rng.integers(-2 ** 20, 2 ** 20, (5, 7)).astype(np.int32)
+    s_w = (rng.random(7) * 1e-3).astype(np.float32)
+    s_x = (rng.random(5) * 1e-2).astype(np.float32)
+    bias = synth.f32_to_bf16_bits(rng.standard_normal(7).astype(np.float32))
+    y = o.epilogue(acc, s_w, s_x, bias)
+    for j in range(7):
+        assert np.array_equal(y[:, j], o.epilogue(acc[:, j:j + 1], s_w[j], s_x, bias[j:j + 1])[:, 0])
+    with pytest.raises(ValueError):
+        o.epilogue(acc, s_w[:5], s_x)
+
+
+def test_linear_int8_per_channel_tolerances():
+    """On a weight whose rows span 2^24 in magnitude, per-channel scales keep
+    every output column accurate; one per-tensor scale does not."""
+    rng = np.random.default_rng(35)
+    layer = synth.TINY
+    xb = layer.x()
+    wb = _rowscaled_weight(layer.n, layer.k, rng)
+    wq, s_w = o.quantize_weights_per_channel(wb, 256, SEED)
+    y, xq, sx, acc = o.linear_int8(xb, wq, s_w, 256, SEED)
+    yb = o.bf16_to_f64(y)
+    assert o.rel_frobenius(yb, o.linear_int8_reference_f64(acc, s_w, sx)) < 2.0 ** -8
+    true = o.bf16_to_f64(xb) @ o.bf16_to_f64(wb).T
+    col_err = np.linalg.norm(yb - true, axis=0) / np.linalg.norm(true, axis=0)
+    assert col_err.max() < 0.05
+    deq = o.dequant_linear_reference_f64(xb, wq, s_w, 256, SEED)
+    assert o.rel_frobenius(deq, true) < 0.05
+    wq_t, s_t = o.quantize_weights(wb, 256, SEED)
+    yt = o.bf16_to_f64(o.linear_int8(xb, wq_t, s_t, 256, SEED)[0])
+    col_err_t = np.linalg.norm(yt - true, axis=0) / np.linalg.norm(true, axis=0)
+    assert col_err_t.max() > 0.5

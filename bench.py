@@ -212,7 +212,21 @@ def main():
         lambda i: cr.convrot_dequant_derotate(wqs[i % nrot_w], s_w, g, seed,
                                               out=outs[i % nrot_w]), reps, stream)
     torch.cuda.synchronize()
-    del wqs, outs
+
+    # ---- per-output-channel weight scales: the same layer, one fp32 scale per
+    # weight row; the int8 forward, its GEMM and the dequant ----
+    wq_pc, sw_pc = cr.convrot_quantize_weights_per_channel(w, g, seed)
+    pc_lin_ms, _, _ = _events_time(
+        lambda i: cr.convrot_linear_int8_per_channel(xs[i % nrot_x], wq_pc, sw_pc, g, seed,
+                                                     workspace=ws, out=y), reps, stream)
+    pc_gemm_ms, _, _ = _events_time(
+        lambda i: cr.convrot_gemm_int8_per_channel(xq, sx, wq_pc, sw_pc, y=y), reps, stream)
+    wqs_pc = [wq_pc] + [wq_pc.clone() for _ in range(nrot_w - 1)]
+    pc_deq_ms, _, _ = _events_time(
+        lambda i: cr.convrot_dequant_derotate_per_channel(wqs_pc[i % nrot_w], sw_pc, g, seed,
+                                                          out=outs[i % nrot_w]), reps, stream)
+    torch.cuda.synchronize()
+    del wqs, outs, wqs_pc, wq_pc
 
     # ---- dequant over the 60-layer stack: 60 + 60 distinct int8 buffers of
     # the two stack shapes, one dequant each per pass, outputs rotated over 4 ----
@@ -286,6 +300,15 @@ def main():
                           "frac_hbm": round(stack_bytes / (stack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "ms_per_pass": round(stack_ms, 4), "bytes": stack_bytes},
         "linear_tops_frac_peak": round(value / PEAK_INT8_TOPS, 4),
+        "per_channel": {
+            "linear_TOPS": round(ops / (pc_lin_ms * 1e-3) / 1e12, 1),
+            "gemm_TOPS": round(ops / (pc_gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_peak": round(ops / (pc_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "dequant_GB/s": round((3.0 * n * k + 4.0 * n) / (pc_deq_ms * 1e-3) / 1e9, 1),
+            "dequant_frac_hbm": round((3.0 * n * k + 4.0 * n) / (pc_deq_ms * 1e-3) / 1e9
+                                      / PEAK_HBM_GBS, 4),
+            "linear_avg_ms": round(pc_lin_ms, 5), "gemm_avg_ms": round(pc_gemm_ms, 5),
+            "dequant_avg_ms": round(pc_deq_ms, 5)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

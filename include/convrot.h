@@ -33,6 +33,17 @@
  *   W_hat = bf16(RN(float(S) * RN(s_w * 2^-log2(sqrt g)))), S = (Wq . D) . H;
  *   y    = bf16(RN(RN(float(acc) * s_w) * s_x[m]) [+ bias[n] in fp32]).
  *
+ * Per-output-channel weight scales (the *_per_channel entry points): s_w is a
+ * vector of n fp32, one per row of W (= per output column of y). Row r of the
+ * rotated weight is quantized with its own amax exactly as a token row is;
+ * the dequant uses RN(s_w[r] * 2^-log2(sqrt g)) for row r and the epilogue
+ * s_w[n] for column n. Published int8 convrot checkpoints carry one scale per
+ * output channel, and a weight scale always multiplies output rows, never the
+ * input axis (PR "share the int8_convrot scheme ... Krea-2 and Z-Image",
+ * "Z-Image: the fused QKV", and the scale-layout fix in its commits: a scale
+ * broadcast along the input axis decodes square weights wrongly).
+ * These vectors must be 16-byte aligned.
+ *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers to row-major, contiguous memory whose
  *     last axis is K (input features). bf16 tensors are passed as uint16_t*.
@@ -49,7 +60,8 @@
  *     N % 16 == 0 and K <= 133144 (int32 accumulator bound) for the GEMM;
  *     all dimensions < 2^31, and ceil(M/128) * ceil(N/128) < 2^31 for the
  *     GEMM. M == 0 is a no-op (the M-sized buffers may then be null).
- *   - Alignment: tensor base pointers 16-byte aligned, scales 4-byte aligned.
+ *   - Alignment: tensor base pointers 16-byte aligned, per-tensor scales and
+ *     s_x 4-byte aligned, per-channel scale vectors 16-byte aligned.
  *   - Results are bit-identical from run to run and independent of slicing.
  */
 #ifndef CONVROT_H
@@ -62,7 +74,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 1
+#define CONVROT_ABI_VERSION 2
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -93,6 +105,19 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int64_t n, int64_t k,
  *   w_out [n, k] bf16 (out)  W_hat = s_w . Wq . blockdiag(R)^T, rounded as above */
 convrot_status convrot_dequant_derotate(const int8_t* wq, const float* s_w, int64_t n, int64_t k,
                                         int g, uint64_t rot_seed, uint16_t* w_out, void* stream);
+
+/* Per-channel variant of convrot_quantize_weights: s_w [n] fp32 (out, 16-byte
+ * aligned), s_w[r] = RN(amax_r / 127) over row r of the rotated weight; row r of
+ * wq is quantized with s_w[r]. Same kernels as convrot_quantize_activations. */
+convrot_status convrot_quantize_weights_per_channel(const uint16_t* w, int64_t n, int64_t k,
+                                                    int g, uint64_t rot_seed, int8_t* wq,
+                                                    float* s_w, void* stream);
+
+/* Per-channel variant of convrot_dequant_derotate: s_w [n] fp32 (in, 16-byte
+ * aligned); row r of w_out is bf16(RN(float(S) * RN(s_w[r] * 2^-log2(sqrt g)))). */
+convrot_status convrot_dequant_derotate_per_channel(const int8_t* wq, const float* s_w, int64_t n,
+                                                    int64_t k, int g, uint64_t rot_seed,
+                                                    uint16_t* w_out, void* stream);
 
 /* Rotate each token row of x by blockdiag(R), take its absmax and quantize it to
  * int8 with one fp32 scale per row (Invoke docs "int8 Compute", introduction).
@@ -127,6 +152,18 @@ convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const 
                                       int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
                                       void* stream);
 
+/* Per-channel variants of the two GEMM calls above: s_w [n] fp32 (in, 16-byte
+ * aligned) and y = bf16(RN(RN(float(acc) s_w[n]) s_x[m]) [+ bias[n]]). */
+convrot_status convrot_gemm_int8_per_channel(const int8_t* xq, const float* s_x,
+                                             const int8_t* wq, const float* s_w,
+                                             const uint16_t* bias, int64_t m, int64_t n,
+                                             int64_t k, uint16_t* y, int32_t* acc, void* stream);
+convrot_status convrot_gemm_int8_per_channel_tile(const int8_t* xq, const float* s_x,
+                                                  const int8_t* wq, const float* s_w,
+                                                  const uint16_t* bias, int64_t m, int64_t n,
+                                                  int64_t k, uint16_t* y, int32_t* acc, int tile,
+                                                  void* stream);
+
 /* The int8_compute forward: for each slice of token rows, rotate + quantize the
  * slice into the workspace, then run the int8 GEMM with the scaling epilogue.
  * Slices hold as many rows as the workspace fits (Invoke docs "int8 Compute",
@@ -141,6 +178,14 @@ convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const fl
                                    const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
                                    uint64_t rot_seed, uint16_t* y, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* Per-channel variant of convrot_linear_int8: s_w [n] fp32 (in, 16-byte
+ * aligned); same slicing and workspace. */
+convrot_status convrot_linear_int8_per_channel(const uint16_t* x, const int8_t* wq,
+                                               const float* s_w, const uint16_t* bias, int64_t m,
+                                               int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                               uint16_t* y, void* workspace,
+                                               size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);

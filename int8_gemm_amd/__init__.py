@@ -21,6 +21,8 @@ __all__ = [
     "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_linear_int8",
     "convrot_linear_int8_workspace_size", "convrot_linear_int8_workspace_for_rows",
     "convrot_rotation_signs", "convrot_abi_version", "convrot_status_string",
+    "convrot_quantize_weights_per_channel", "convrot_dequant_derotate_per_channel",
+    "convrot_gemm_int8_per_channel", "convrot_linear_int8_per_channel",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,8 +37,11 @@ EXPORTED_SYMBOLS = (
     "convrot_quantize_weights", "convrot_dequant_derotate", "convrot_quantize_activations",
     "convrot_quantize_activations_exact", "convrot_gemm_int8", "convrot_gemm_int8_tile",
     "convrot_linear_int8", "convrot_linear_int8_workspace_for_rows",
-    "convrot_linear_int8_workspace_size", "convrot_rotation_signs", "convrot_status_string", "convrot_last_error_string",
-    "convrot_abi_version",
+    "convrot_linear_int8_workspace_size", "convrot_rotation_signs", "convrot_status_string",
+    "convrot_last_error_string", "convrot_abi_version",
+    "convrot_quantize_weights_per_channel", "convrot_dequant_derotate_per_channel",
+    "convrot_gemm_int8_per_channel", "convrot_gemm_int8_per_channel_tile",
+    "convrot_linear_int8_per_channel",
 )
 
 _STATUS = {0: "CONVROT_OK", 1: "CONVROT_E_INVALID_ARG", 2: "CONVROT_E_UNSUPPORTED_GROUP",
@@ -79,6 +84,11 @@ def load_library():
             "convrot_gemm_int8_tile": [P, P, P, P, P, I64, I64, I64, P, P, I, P],
             "convrot_linear_int8": [P, P, P, P, I64, I64, I64, I, U64, P, P, SZ, P],
             "convrot_rotation_signs": [U64, I, P],
+            "convrot_quantize_weights_per_channel": [P, I64, I64, I, U64, P, P, P],
+            "convrot_dequant_derotate_per_channel": [P, P, I64, I64, I, U64, P, P],
+            "convrot_gemm_int8_per_channel": [P, P, P, P, P, I64, I64, I64, P, P, P],
+            "convrot_gemm_int8_per_channel_tile": [P, P, P, P, P, I64, I64, I64, P, P, I, P],
+            "convrot_linear_int8_per_channel": [P, P, P, P, I64, I64, I64, I, U64, P, P, SZ, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -146,33 +156,62 @@ def convrot_rotation_signs(rot_seed: int, g: int) -> list[int]:
     return list(buf)
 
 
-def convrot_quantize_weights(w: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
-                             wq: torch.Tensor | None = None, s_w: torch.Tensor | None = None):
-    """W bf16 [n, k] -> (Wq int8 [n, k], s_w fp32 [1])."""
+def _need_sw(s_w: torch.Tensor, per_channel: bool, n: int):
+    _need(s_w, "s_w", torch.float32, 1 if per_channel else None)
+    if per_channel and s_w.shape[0] != n:
+        raise ValueError(f"per-channel s_w needs {n} entries (got {s_w.shape[0]})")
+
+
+def _quant_w(fn_name, per_channel, w, g, rot_seed, wq, s_w):
     _need(w, "w", torch.bfloat16, 2)
     n, k = w.shape
     wq = torch.empty((n, k), dtype=torch.int8, device=w.device) if wq is None else wq
-    s_w = torch.empty(1, dtype=torch.float32, device=w.device) if s_w is None else s_w
+    if s_w is None:
+        s_w = torch.empty(n if per_channel else 1, dtype=torch.float32, device=w.device)
     _need(wq, "wq", torch.int8, 2)
-    _need(s_w, "s_w", torch.float32)
+    _need_sw(s_w, per_channel, n)
     _same_device(w, wq, s_w)
-    _check(load_library().convrot_quantize_weights(_ptr(w), n, k, g, rot_seed, _ptr(wq),
-                                                   _ptr(s_w), _stream(w)))
+    _check(getattr(load_library(), fn_name)(_ptr(w), n, k, g, rot_seed, _ptr(wq), _ptr(s_w),
+                                            _stream(w)))
     return wq, s_w
+
+
+def convrot_quantize_weights(w: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                             wq: torch.Tensor | None = None, s_w: torch.Tensor | None = None):
+    """W bf16 [n, k] -> (Wq int8 [n, k], s_w fp32 [1])."""
+    return _quant_w("convrot_quantize_weights", False, w, g, rot_seed, wq, s_w)
+
+
+def convrot_quantize_weights_per_channel(w: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                                         wq: torch.Tensor | None = None,
+                                         s_w: torch.Tensor | None = None):
+    """W bf16 [n, k] -> (Wq int8 [n, k], s_w fp32 [n]), one scale per output row."""
+    return _quant_w("convrot_quantize_weights_per_channel", True, w, g, rot_seed, wq, s_w)
+
+
+def _dequant(fn_name, per_channel, wq, s_w, g, rot_seed, out):
+    _need(wq, "wq", torch.int8, 2)
+    n, k = wq.shape
+    _need_sw(s_w, per_channel, n)
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=wq.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(wq, s_w, out)
+    _check(getattr(load_library(), fn_name)(_ptr(wq), _ptr(s_w), n, k, g, rot_seed, _ptr(out),
+                                            _stream(wq)))
+    return out
 
 
 def convrot_dequant_derotate(wq: torch.Tensor, s_w: torch.Tensor, g: int,
                              rot_seed: int = ROT_SEED, *, out: torch.Tensor | None = None):
     """Wq int8 [n, k], s_w fp32 [1] -> W_hat bf16 [n, k]."""
-    _need(wq, "wq", torch.int8, 2)
-    _need(s_w, "s_w", torch.float32)
-    n, k = wq.shape
-    out = torch.empty((n, k), dtype=torch.bfloat16, device=wq.device) if out is None else out
-    _need(out, "out", torch.bfloat16, 2)
-    _same_device(wq, s_w, out)
-    _check(load_library().convrot_dequant_derotate(_ptr(wq), _ptr(s_w), n, k, g, rot_seed,
-                                                   _ptr(out), _stream(wq)))
-    return out
+    return _dequant("convrot_dequant_derotate", False, wq, s_w, g, rot_seed, out)
+
+
+def convrot_dequant_derotate_per_channel(wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                                         rot_seed: int = ROT_SEED, *,
+                                         out: torch.Tensor | None = None):
+    """Wq int8 [n, k], s_w fp32 [n] -> W_hat bf16 [n, k] (row r scaled by s_w[r])."""
+    return _dequant("convrot_dequant_derotate_per_channel", True, wq, s_w, g, rot_seed, out)
 
 
 def _quant_act(fn_name, x, g, rot_seed, xq, s_x):
@@ -202,18 +241,13 @@ def convrot_quantize_activations_exact(x: torch.Tensor, g: int, rot_seed: int = 
     return _quant_act("convrot_quantize_activations_exact", x, g, rot_seed, xq, s_x)
 
 
-def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
-                      bias: torch.Tensor | None = None, *, want_y: bool = True,
-                      want_acc: bool = False, y: torch.Tensor | None = None,
-                      acc: torch.Tensor | None = None, tile: int = 0):
-    """int8 GEMM + epilogue. Returns (y bf16 [m, n] or None, acc int32 [m, n] or None).
-    `tile` != 0 forces the block tile (test / tuning hook convrot_gemm_int8_tile)."""
+def _gemm(per_channel, xq, s_x, wq, s_w, bias, want_y, want_acc, y, acc, tile):
     _need(xq, "xq", torch.int8, 2)
     _need(wq, "wq", torch.int8, 2)
     _need(s_x, "s_x", torch.float32, 1)
-    _need(s_w, "s_w", torch.float32)
     m, k = xq.shape
     n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
     if wq.shape[1] != k:
         raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
     if bias is not None:
@@ -228,14 +262,33 @@ def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w
         _need(acc, "acc", torch.int32, 2)
     _same_device(xq, s_x, wq, s_w, bias, y, acc)
     lib = load_library()
+    name = "convrot_gemm_int8_per_channel" if per_channel else "convrot_gemm_int8"
+    args = [_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k, _ptr(y), _ptr(acc)]
     if tile:
-        st = lib.convrot_gemm_int8_tile(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(bias), m,
-                                        n, k, _ptr(y), _ptr(acc), tile, _stream(xq))
+        st = getattr(lib, name + "_tile")(*args, tile, _stream(xq))
     else:
-        st = lib.convrot_gemm_int8(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k,
-                                   _ptr(y), _ptr(acc), _stream(xq))
+        st = getattr(lib, name)(*args, _stream(xq))
     _check(st)
     return y, acc
+
+
+def convrot_gemm_int8(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
+                      bias: torch.Tensor | None = None, *, want_y: bool = True,
+                      want_acc: bool = False, y: torch.Tensor | None = None,
+                      acc: torch.Tensor | None = None, tile: int = 0):
+    """int8 GEMM + epilogue. Returns (y bf16 [m, n] or None, acc int32 [m, n] or None).
+    `tile` != 0 forces the block tile (test / tuning hook convrot_gemm_int8_tile)."""
+    return _gemm(False, xq, s_x, wq, s_w, bias, want_y, want_acc, y, acc, tile)
+
+
+def convrot_gemm_int8_per_channel(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor,
+                                  s_w: torch.Tensor, bias: torch.Tensor | None = None, *,
+                                  want_y: bool = True, want_acc: bool = False,
+                                  y: torch.Tensor | None = None, acc: torch.Tensor | None = None,
+                                  tile: int = 0):
+    """convrot_gemm_int8 with s_w fp32 [n]: column n of y uses s_w[n]. `tile` != 0
+    calls the hook convrot_gemm_int8_per_channel_tile."""
+    return _gemm(True, xq, s_x, wq, s_w, bias, want_y, want_acc, y, acc, tile)
 
 
 def convrot_linear_int8_workspace_size(m: int, n: int, k: int) -> int:
@@ -246,16 +299,12 @@ def convrot_linear_int8_workspace_for_rows(rows: int, k: int) -> int:
     return int(load_library().convrot_linear_int8_workspace_for_rows(rows, k))
 
 
-def convrot_linear_int8(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
-                        rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
-                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
-    """The int8_compute forward: x bf16 [m, k] -> y bf16 [m, n]. `workspace`
-    (uint8 on the device) defaults to the library's default size."""
+def _linear(fn_name, per_channel, x, wq, s_w, g, rot_seed, bias, workspace, out):
     _need(x, "x", torch.bfloat16, 2)
     _need(wq, "wq", torch.int8, 2)
-    _need(s_w, "s_w", torch.float32)
     m, k = x.shape
     n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, 1)
     if workspace is None:
@@ -265,7 +314,24 @@ def convrot_linear_int8(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g:
     out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device) if out is None else out
     _need(out, "out", torch.bfloat16, 2)
     _same_device(x, wq, s_w, bias, workspace, out)
-    _check(load_library().convrot_linear_int8(_ptr(x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k,
-                                              g, rot_seed, _ptr(out), _ptr(workspace),
-                                              workspace.numel(), _stream(x)))
+    _check(getattr(load_library(), fn_name)(_ptr(x), _ptr(wq), _ptr(s_w), _ptr(bias), m, n, k,
+                                            g, rot_seed, _ptr(out), _ptr(workspace),
+                                            workspace.numel(), _stream(x)))
     return out
+
+
+def convrot_linear_int8(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                        rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The int8_compute forward: x bf16 [m, k] -> y bf16 [m, n]. `workspace`
+    (uint8 on the device) defaults to the library's default size."""
+    return _linear("convrot_linear_int8", False, x, wq, s_w, g, rot_seed, bias, workspace, out)
+
+
+def convrot_linear_int8_per_channel(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                                    rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                                    workspace: torch.Tensor | None = None,
+                                    out: torch.Tensor | None = None):
+    """convrot_linear_int8 with per-channel weight scales s_w fp32 [n]."""
+    return _linear("convrot_linear_int8_per_channel", True, x, wq, s_w, g, rot_seed, bias,
+                   workspace, out)

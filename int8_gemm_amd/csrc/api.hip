@@ -102,6 +102,11 @@ convrot_status check_gemm(const char* fn, int64_t m, int64_t n, int64_t k) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Per-tensor s_w: one fp32, 4-byte aligned. Per-channel s_w: n fp32, 16-byte
+// aligned (the GEMM epilogue reads four consecutive scales at once).
+size_t sw_bytes(bool pc, int64_t n) { return pc ? (size_t)n * 4 : 4; }
+bool sw_aligned(bool pc, const float* s_w) { return aligned(s_w, pc ? 16 : 4); }
+
 }  // namespace
 
 extern "C" {
@@ -132,37 +137,67 @@ convrot_status convrot_rotation_signs(uint64_t rot_seed, int g, int8_t* d) {
   return ok();
 }
 
-convrot_status convrot_quantize_weights(const uint16_t* w, int64_t n, int64_t k, int g,
-                                        uint64_t rot_seed, int8_t* wq, float* s_w,
-                                        void* stream) {
-  const char* fn = "convrot_quantize_weights";
+static convrot_status quantize_weights_impl(const char* fn, bool pc, const uint16_t* w,
+                                            int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                            int8_t* wq, float* s_w, void* stream) {
   if (!w || !wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
   if (convrot_status s = check_rot(fn, n, k, g)) return s;
-  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s_w, 4))
+  if (!aligned(w, 16) || !aligned(wq, 16) || !sw_aligned(pc, s_w))
     return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  const size_t nsw = sw_bytes(pc, n);
   if (overlap(w, (size_t)(n * k) * 2, wq, (size_t)(n * k)) ||
-      overlap(w, (size_t)(n * k) * 2, s_w, 4) || overlap(wq, (size_t)(n * k), s_w, 4))
+      overlap(w, (size_t)(n * k) * 2, s_w, nsw) || overlap(wq, (size_t)(n * k), s_w, nsw))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   const SignMask sm = make_signs(rot_seed, g);
-  return hip_status(launch_quantize_tensor(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream),
-                    fn);
+  // per channel, a weight row is quantized exactly as a token row is
+  const hipError_t e =
+      pc ? launch_quantize_rows(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream)
+         : launch_quantize_tensor(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+convrot_status convrot_quantize_weights(const uint16_t* w, int64_t n, int64_t k, int g,
+                                        uint64_t rot_seed, int8_t* wq, float* s_w,
+                                        void* stream) {
+  return quantize_weights_impl("convrot_quantize_weights", false, w, n, k, g, rot_seed, wq, s_w,
+                               stream);
+}
+
+convrot_status convrot_quantize_weights_per_channel(const uint16_t* w, int64_t n, int64_t k,
+                                                    int g, uint64_t rot_seed, int8_t* wq,
+                                                    float* s_w, void* stream) {
+  return quantize_weights_impl("convrot_quantize_weights_per_channel", true, w, n, k, g, rot_seed,
+                               wq, s_w, stream);
+}
+
+static convrot_status dequant_impl(const char* fn, bool pc, const int8_t* wq, const float* s_w,
+                                   int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                   uint16_t* w_out, void* stream) {
+  if (!wq || !s_w || !w_out) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
+  if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
+  if (convrot_status s = check_rot(fn, n, k, g)) return s;
+  if (!aligned(wq, 16) || !aligned(w_out, 16) || !sw_aligned(pc, s_w))
+    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
+  if (overlap(wq, (size_t)(n * k), w_out, (size_t)(n * k) * 2) ||
+      overlap(s_w, sw_bytes(pc, n), w_out, (size_t)(n * k) * 2))
+    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
+  const SignMask sm = make_signs(rot_seed, g);
+  return hip_status(launch_dequant(wq, s_w, pc, n, k, g, sm, w_out, (hipStream_t)stream), fn);
 }
 
 convrot_status convrot_dequant_derotate(const int8_t* wq, const float* s_w, int64_t n, int64_t k,
                                         int g, uint64_t rot_seed, uint16_t* w_out,
                                         void* stream) {
-  const char* fn = "convrot_dequant_derotate";
-  if (!wq || !s_w || !w_out) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
-  if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
-  if (convrot_status s = check_rot(fn, n, k, g)) return s;
-  if (!aligned(wq, 16) || !aligned(w_out, 16) || !aligned(s_w, 4))
-    return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
-  if (overlap(wq, (size_t)(n * k), w_out, (size_t)(n * k) * 2) ||
-      overlap(s_w, 4, w_out, (size_t)(n * k) * 2))
-    return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
-  const SignMask sm = make_signs(rot_seed, g);
-  return hip_status(launch_dequant(wq, s_w, n, k, g, sm, w_out, (hipStream_t)stream), fn);
+  return dequant_impl("convrot_dequant_derotate", false, wq, s_w, n, k, g, rot_seed, w_out,
+                      stream);
+}
+
+convrot_status convrot_dequant_derotate_per_channel(const int8_t* wq, const float* s_w, int64_t n,
+                                                    int64_t k, int g, uint64_t rot_seed,
+                                                    uint16_t* w_out, void* stream) {
+  return dequant_impl("convrot_dequant_derotate_per_channel", true, wq, s_w, n, k, g, rot_seed,
+                      w_out, stream);
 }
 
 static convrot_status quantize_activations_impl(const char* fn, bool exact, const uint16_t* x,
@@ -199,7 +234,7 @@ convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, 
                                    rot_seed, xq, s_x, stream);
 }
 
-static convrot_status gemm_impl(const char* fn, const int8_t* xq, const float* s_x,
+static convrot_status gemm_impl(const char* fn, bool pc, const int8_t* xq, const float* s_x,
                                 const int8_t* wq, const float* s_w, const uint16_t* bias,
                                 int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc,
                                 int tile, void* stream) {
@@ -209,31 +244,52 @@ static convrot_status gemm_impl(const char* fn, const int8_t* xq, const float* s
   if (convrot_status s = check_gemm(fn, m, n, k)) return s;
   if (m == 0) return ok();  // the M-sized buffers may be null
   if (!xq || !s_x || (!y && !acc)) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
-  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(s_x, 4) || !aligned(s_w, 4) ||
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(s_x, 4) || !sw_aligned(pc, s_w) ||
       (bias && !aligned(bias, 8)) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
     return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
   const size_t ny = (size_t)(m * n) * 2, na = (size_t)(m * n) * 4;
   if (overlap(y, ny, xq, (size_t)(m * k)) || overlap(y, ny, wq, (size_t)(n * k)) ||
       overlap(acc, na, xq, (size_t)(m * k)) || overlap(acc, na, wq, (size_t)(n * k)) ||
-      overlap(y, ny, acc, na))
+      overlap(y, ny, acc, na) || overlap(y, ny, s_w, sw_bytes(pc, n)) ||
+      overlap(acc, na, s_w, sw_bytes(pc, n)))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   if (m == 0) return ok();
-  return hip_status(
-      launch_gemm_tile(xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile, (hipStream_t)stream), fn);
+  return hip_status(launch_gemm_tile(xq, s_x, wq, s_w, pc, bias, m, n, k, y, acc, tile,
+                                     (hipStream_t)stream),
+                    fn);
 }
 
 convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
                                  int64_t k, uint16_t* y, int32_t* acc, void* stream) {
-  return gemm_impl("convrot_gemm_int8", xq, s_x, wq, s_w, bias, m, n, k, y, acc, 0, stream);
+  return gemm_impl("convrot_gemm_int8", false, xq, s_x, wq, s_w, bias, m, n, k, y, acc, 0,
+                   stream);
+}
+
+convrot_status convrot_gemm_int8_per_channel(const int8_t* xq, const float* s_x,
+                                             const int8_t* wq, const float* s_w,
+                                             const uint16_t* bias, int64_t m, int64_t n,
+                                             int64_t k, uint16_t* y, int32_t* acc,
+                                             void* stream) {
+  return gemm_impl("convrot_gemm_int8_per_channel", true, xq, s_x, wq, s_w, bias, m, n, k, y, acc,
+                   0, stream);
 }
 
 convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
                                       const float* s_w, const uint16_t* bias, int64_t m,
                                       int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
                                       void* stream) {
-  return gemm_impl("convrot_gemm_int8_tile", xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile,
+  return gemm_impl("convrot_gemm_int8_tile", false, xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile,
                    stream);
+}
+
+convrot_status convrot_gemm_int8_per_channel_tile(const int8_t* xq, const float* s_x,
+                                                  const int8_t* wq, const float* s_w,
+                                                  const uint16_t* bias, int64_t m, int64_t n,
+                                                  int64_t k, uint16_t* y, int32_t* acc, int tile,
+                                                  void* stream) {
+  return gemm_impl("convrot_gemm_int8_per_channel_tile", true, xq, s_x, wq, s_w, bias, m, n, k, y,
+                   acc, tile, stream);
 }
 
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k) {
@@ -248,17 +304,16 @@ size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k) {
   return convrot_linear_int8_workspace_for_rows(rows, k);
 }
 
-convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const float* s_w,
-                                   const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
-                                   uint64_t rot_seed, uint16_t* y, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  const char* fn = "convrot_linear_int8";
+static convrot_status linear_impl(const char* fn, bool pc, const uint16_t* x, const int8_t* wq,
+                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                                  int64_t k, int g, uint64_t rot_seed, uint16_t* y,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (convrot_status s = check_rot(fn, m, k, g)) return s;
   if (convrot_status s = check_gemm(fn, m, n, k)) return s;
   if (m == 0) return ok();  // the M-sized buffers may be null
   if (!x || !y || !workspace) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
-  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(s_w, 4) || !aligned(y, 16) ||
+  if (!aligned(x, 16) || !aligned(wq, 16) || !sw_aligned(pc, s_w) || !aligned(y, 16) ||
       (bias && !aligned(bias, 8)) || !aligned(workspace, 256))
     return fail(CONVROT_E_MISALIGNED, "%s: misaligned pointer", fn);
   // largest slice that fits: align256(r*k) + 4r <= bytes
@@ -272,7 +327,8 @@ convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const fl
   if (overlap(y, ny, x, (size_t)(m * k) * 2) || overlap(y, ny, wq, (size_t)(n * k)) ||
       overlap(y, ny, workspace, workspace_bytes) ||
       overlap(workspace, workspace_bytes, x, (size_t)(m * k) * 2) ||
-      overlap(workspace, workspace_bytes, wq, (size_t)(n * k)))
+      overlap(workspace, workspace_bytes, wq, (size_t)(n * k)) ||
+      overlap(y, ny, s_w, sw_bytes(pc, n)) || overlap(workspace, workspace_bytes, s_w, sw_bytes(pc, n)))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   if (m == 0) return ok();
   // whole GEMM tiles per slice when the workspace allows
@@ -287,10 +343,27 @@ convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const fl
     const int64_t rows = (m - r0) < slice ? (m - r0) : slice;
     hipError_t e = launch_quantize_rows(x + r0 * k, xq, sx, rows, (int)k, g, sm, st);
     if (e != hipSuccess) return hip_status(e, fn);
-    e = launch_gemm(xq, sx, wq, s_w, bias, rows, n, k, y + r0 * n, nullptr, st);
+    e = launch_gemm(xq, sx, wq, s_w, pc, bias, rows, n, k, y + r0 * n, nullptr, st);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const float* s_w,
+                                   const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
+                                   uint64_t rot_seed, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return linear_impl("convrot_linear_int8", false, x, wq, s_w, bias, m, n, k, g, rot_seed, y,
+                     workspace, workspace_bytes, stream);
+}
+
+convrot_status convrot_linear_int8_per_channel(const uint16_t* x, const int8_t* wq,
+                                               const float* s_w, const uint16_t* bias, int64_t m,
+                                               int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                               uint16_t* y, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  return linear_impl("convrot_linear_int8_per_channel", true, x, wq, s_w, bias, m, n, k, g,
+                     rot_seed, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,10 @@
 // needs only the g/32 blocks d-scaled H_32 and their negatives, built once
 // per lane from the sign mask. For g < 32 the A operand is block-diagonal.
 // The kernel is bound by HBM: 1 byte read and 2 bytes written per element.
+//
+// Per-channel scales (one s_w per weight row): a weight row holds K/R whole
+// view rows, so the scale is a per-lane value: lane jl of a tile decodes view
+// row jl, whose weight row is (tile*32 + jl) / (K/R).
 
 #include "common.h"
 #include "internal.h"
@@ -52,10 +56,11 @@ __device__ __forceinline__ v4i frag_from_masks(uint32_t neg, uint32_t nz) {
   return f;
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__ wq,
+template <int G, bool PC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1))) void dequant_kernel(const int8_t* __restrict__ wq,
                                                       const float* __restrict__ s_w,
-                                                      int64_t nrows, SignMask sm,
+                                                      int64_t nrows, int vrows_per_ch,
+                                                      double inv_vrows_per_ch, SignMask sm,
                                                       uint16_t* __restrict__ out) {
   constexpr int R = G > 32 ? G : 32;   // bytes per view row
   constexpr int NB = R / 32;           // 32-blocks per view row
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
     fragN[0] = fragP[0];
   }
 
-  const float c = *s_w * (1.0f / (float)(1 << KS));
+  const float c_t = PC ? 0.0f : *s_w * (1.0f / (float)(1 << KS));
   const int64_t ntiles = (nrows + 31) / 32;
   const int64_t nchunks = (ntiles + TPB - 1) / TPB;
   const int64_t in_bytes = nrows * R;
@@ -145,6 +150,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
     load_chunk(ch + gridDim.x, pre);  // next chunk, in flight during this one
 
     const int64_t tile = ch * TPB + tl;
+    float c = c_t;
+    if constexpr (PC) {
+      // weight row of view row vr: q = vr / vrows_per_ch from a float64
+      // estimate (vr < 2^53), corrected by one either way
+      const int64_t vr = tile * 32 + jl < nrows ? tile * 32 + jl : nrows - 1;
+      int64_t q = (int64_t)((double)vr * inv_vrows_per_ch);
+      if (q * vrows_per_ch > vr) --q;
+      if ((q + 1) * vrows_per_ch <= vr) ++q;
+      c = s_w[q] * (1.0f / (float)(1 << KS));
+    }
     v4i bfr[NB];
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
@@ -195,8 +210,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t k, int g,
-                          const SignMask& sm, uint16_t* w_out, hipStream_t st) {
+template <int G>
+static void launch_g(bool pc, int64_t blocks, const int8_t* wq, const float* s_w, int64_t nrows,
+                     int vrows_per_ch, const SignMask& sm, uint16_t* w_out, hipStream_t st) {
+  auto kern = pc ? dequant_kernel<G, true> : dequant_kernel<G, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w, nrows,
+                     vrows_per_ch, 1.0 / (double)vrows_per_ch, sm, w_out);
+}
+
+hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,
+                          int64_t k, int g, const SignMask& sm, uint16_t* w_out, hipStream_t st) {
   const int64_t ne = n * k;
   if (ne == 0) return hipSuccess;
   const int R = g > 32 ? g : 32;
@@ -209,23 +232,12 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, int64_t n, int64_t
 #endif
   const int64_t cap = (int64_t)kNumCUs * CONVROT_DEQUANT_BLOCKS_PER_CU;  // persistent blocks
   const int64_t blocks = chunks < cap ? chunks : cap;
+  const int vrows_per_ch = (int)(k / R);  // K % R == 0 for every supported (K, g)
   switch (g) {
-    case 4:
-      hipLaunchKernelGGL(dequant_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w,
-                         nrows, sm, w_out);
-      break;
-    case 16:
-      hipLaunchKernelGGL(dequant_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w,
-                         nrows, sm, w_out);
-      break;
-    case 64:
-      hipLaunchKernelGGL(dequant_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w,
-                         nrows, sm, w_out);
-      break;
-    default:
-      hipLaunchKernelGGL(dequant_kernel<256>, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w,
-                         nrows, sm, w_out);
-      break;
+    case 4: launch_g<4>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 16: launch_g<16>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 64: launch_g<64>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    default: launch_g<256>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
   }
   return hipGetLastError();
 }

@@ -79,7 +79,9 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP>
+// PC: s_w holds one scale per output column n (per output channel of the
+// weight) instead of one for the tensor.
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP, bool PC>
 __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_x, const int8_t* __restrict__ wq,
     const float* __restrict__ s_w, const uint16_t* __restrict__ bias, int M, int N, int K,
@@ -345,7 +347,21 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
 
   // ---- epilogue: 32x32 output layout: lane holds m = lane % 32 of the
   // tile and n = 8*a + 4*(lane/32) + e for register 4a + e ----
-  const float sw = *s_w;
+  const float sw = PC ? 0.0f : *s_w;
+  // per-channel: the 4 consecutive columns of each (i, a) register group,
+  // loaded once for all NJ row blocks
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  f4 swc[PC ? NI : 1][4];
+  if constexpr (PC) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int n = n0 + wn * WTN + i * 32 + 8 * a + 4 * fh;
+        swc[i][a] = n < N ? *reinterpret_cast<const f4*>(s_w + n) : (f4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int m = m0 + wm * WTM + j * 32 + fr;
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
         float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          f[e] = (float)v[4 * a + e] * sw;
+          f[e] = (float)v[4 * a + e] * (PC ? swc[PC ? i : 0][a][e] : sw);
           f[e] = f[e] * sx;
         }
         if (bias) {
@@ -388,13 +404,13 @@ struct TileCfg {
   int bm, bn, ns, per_cu;
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
+template <bool PC, int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
 hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                       const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
                       hipStream_t st) {
   constexpr int lds_bytes = NS * (BM + BN) * BK;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
-  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP>;
+  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP, PC>;
   static bool attr = false;  // benign race: the call is idempotent
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -438,40 +454,43 @@ TileCfg choose_tile(int64_t m, int64_t n) {
 // 128-byte K-steps (whole L2 lines per request): a two-stage ring for the
 // 256 and 128 tiles (64 and 32 KB stages), three stages and four producer
 // waves for the 192 tile. Otherwise 64-byte K-steps with deeper rings.
+template <bool PC>
 static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
                               const float* s_w, const uint16_t* bias, int M, int N, int K,
                               uint16_t* y, int32_t* acc, hipStream_t st) {
   switch (tile) {
     case 256:
       if (K % 128 == 0)
-        return launch_cfg<256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     case 192:
       if (K % 128 == 0)
-        return launch_cfg<192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
+        return launch_cfg<PC, 192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
                                                           st);
-      return launch_cfg<192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, 192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     default:
       if (K % 128 == 0)
-        return launch_cfg<128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, 128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, 128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
   }
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
-                       const uint16_t* bias, int64_t m, int64_t n, int64_t k, uint16_t* y,
-                       int32_t* acc, hipStream_t st) {
-  if (m == 0 || n == 0) return hipSuccess;
-  return launch_tile(choose_tile(m, n).bm, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc,
-                     st);
+                       bool sw_per_channel, const uint16_t* bias, int64_t m, int64_t n, int64_t k,
+                       uint16_t* y, int32_t* acc, hipStream_t st) {
+  return launch_gemm_tile(xq, s_x, wq, s_w, sw_per_channel, bias, m, n, k, y, acc, 0, st);
 }
 
 hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
-                            const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
-                            int64_t k, uint16_t* y, int32_t* acc, int tile, hipStream_t st) {
+                            const float* s_w, bool sw_per_channel, const uint16_t* bias,
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
+                            hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (tile == 0) return launch_gemm(xq, s_x, wq, s_w, bias, m, n, k, y, acc, st);
-  return launch_tile(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st);
+  if (tile == 0) tile = choose_tile(m, n).bm;
+  return sw_per_channel
+             ? launch_tile<true>(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st)
+             : launch_tile<false>(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc,
+                                  st);
 }
 
 }  // namespace convrot

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 1
+    assert cr.convrot_abi_version() == 2
     for s in range(7):
         assert cr.convrot_status_string(s)
 
@@ -73,6 +73,10 @@ def test_rotating_entry_points_reject_bad_group_and_shape(lib, g, k, want):
                    ctypes.c_void_p(1 << 28), None) == want
     assert _status(lib, "convrot_dequant_derotate", FAKE, ctypes.c_void_p(1 << 24), 8, k, g, 1,
                    ctypes.c_void_p(1 << 28), None) == want
+    assert _status(lib, "convrot_quantize_weights_per_channel", FAKE, 8, k, g, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28), None) == want
+    assert _status(lib, "convrot_dequant_derotate_per_channel", FAKE, ctypes.c_void_p(1 << 24), 8,
+                   k, g, 1, ctypes.c_void_p(1 << 28), None) == want
     assert lib.convrot_last_error_string()
 
 
@@ -138,3 +142,41 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros((4, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         cr.convrot_quantize_activations(x, 256)
+
+
+def test_per_channel_scale_vector_checks(lib):
+    """A per-channel s_w is n floats, 16-byte aligned, and may not overlap an
+    output; every check fires before any HIP call."""
+    sw_mis = ctypes.c_void_p((1 << 26) + 4)     # 4-byte aligned only
+    n, k = 64, 256
+    assert _status(lib, "convrot_quantize_weights_per_channel", FAKE, n, k, 256, 1,
+                   ctypes.c_void_p(1 << 24), sw_mis, None) == 4
+    assert _status(lib, "convrot_dequant_derotate_per_channel", FAKE, sw_mis, n, k, 256, 1,
+                   ctypes.c_void_p(1 << 28), None) == 4
+    for fn in ("convrot_gemm_int8_per_channel",):
+        assert _status(lib, fn, FAKE, ctypes.c_void_p(1 << 22), ctypes.c_void_p(1 << 24), sw_mis,
+                       None, 8, n, k, ctypes.c_void_p(1 << 28), None, None) == 4
+    assert _status(lib, "convrot_gemm_int8_per_channel_tile", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), sw_mis, None, 8, n, k, ctypes.c_void_p(1 << 28),
+                   None, 192, None) == 4
+    assert _status(lib, "convrot_linear_int8_per_channel", FAKE, ctypes.c_void_p(1 << 24), sw_mis,
+                   None, 8, n, k, 256, 1, ctypes.c_void_p(1 << 28), ctypes.c_void_p(1 << 32),
+                   1 << 20, None) == 4
+    # the n-float vector overlapping y (y at 1 << 28, s_w n*4 bytes just below its end)
+    y_end = (1 << 28) + 8 * n * 2
+    sw_in_y = ctypes.c_void_p(y_end - 16)
+    assert _status(lib, "convrot_gemm_int8_per_channel", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), sw_in_y, None, 8, n, k, ctypes.c_void_p(1 << 28),
+                   None, None) == 1
+    # ... and starting just below y: only the vector's length makes it overlap
+    sw_before_y = ctypes.c_void_p((1 << 28) - 16)
+    assert _status(lib, "convrot_gemm_int8_per_channel", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), sw_before_y, None, 8, n, k,
+                   ctypes.c_void_p(1 << 28), None, None) == 1
+    # the per-channel quantize writes n scales: overlapping wq is rejected
+    assert _status(lib, "convrot_quantize_weights_per_channel", FAKE, n, k, 256, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p((1 << 24) + n * k - 16), None) == 1
+    # m == 0 is a no-op here too
+    assert _status(lib, "convrot_gemm_int8_per_channel", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 0, n, k,
+                   ctypes.c_void_p(1 << 28), None, None) == 0

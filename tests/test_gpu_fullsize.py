@@ -113,9 +113,10 @@ def test_fullsize(layer, g):
     for r0 in range(0, m, 4096):  # exact: integer partial sums below 2^53
         want = xq[r0:r0 + 4096].cpu().numpy().astype(np.float64) @ wcols
         assert np.array_equal(got[r0:r0 + 4096], want.astype(np.int64)), f"rows {r0}.."
-    # and the epilogue of the same launch on those columns
-    y_cols = oracle.epilogue(got.astype(np.int64), s_ref, s_x.cpu().numpy())
-    assert np.array_equal(host_bits(y2[:, cols_t].contiguous()), y_cols)
+    # and the epilogue of the same launch on those columns, at the sampled
+    # token rows (oracle operands only)
+    y_cols = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref[cols]), s_ref, sx_ref)
+    assert np.array_equal(host_bits(y2[rows_t][:, cols_t].contiguous()), y_cols)
 
 
 def test_dequant_stack_layers_0_and_59():
@@ -135,3 +136,34 @@ def test_dequant_stack_layers_0_and_59():
             out = cr.convrot_dequant_derotate(copies[li], s_w, g, SEED)
             assert np.array_equal(host_bits(out), want), li
         del copies
+
+
+def test_fullsize_per_channel_zimage_attn():
+    """Per-channel scales at the full Z-Image attention shape: the weight
+    quantization in full, the dequant on sampled weight rows, the int8 forward
+    on sampled token rows, every column."""
+    layer, g = synth.ZIMAGE_ATTN, 256
+    m, n = layer.m, layer.n
+    print(f"full-size per-channel {layer.name}: quantize_weights", flush=True)
+    e = np.random.default_rng(5).integers(-12, 13, n)
+    wb = synth.f32_to_bf16_bits((oracle.bf16_to_f64(layer.w()) * 2.0 ** e[:, None])
+                                .astype(np.float32))
+    wq, s_w = cr.convrot_quantize_weights_per_channel(dev_bf16(wb), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights_per_channel(wb, g, SEED)
+    assert np.array_equal(f32_bits(s_w.cpu().numpy()), f32_bits(s_ref))
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+
+    print(f"full-size per-channel {layer.name}: dequant", flush=True)
+    nrows = sample_rows(n, n_random=24)
+    w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
+    assert np.array_equal(host_bits(w_hat[torch.from_numpy(nrows).to(DEV)]),
+                          oracle.dequant_derotate(wq_ref[nrows], s_ref[nrows], g, SEED))
+    del w_hat
+
+    print(f"full-size per-channel {layer.name}: linear_int8", flush=True)
+    xb = layer.x()
+    y = cr.convrot_linear_int8_per_channel(dev_bf16(xb), wq, s_w, g, SEED)
+    rows = sample_rows(m, extra=(2 * n - 1, 2 * n))
+    xq_ref, sx_ref = oracle.quantize_activations(xb[rows], g, SEED)
+    y_ref = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref)
+    assert np.array_equal(host_bits(y[torch.from_numpy(rows).to(DEV)]), y_ref)

@@ -259,3 +259,137 @@ def test_wrong_rotation_gives_noise():
         return float((a * b).sum() / math.sqrt((a * a).sum() * (b * b).sum()))
     assert cos(good, w) > 0.9999
     assert abs(cos(bad, w)) < 0.3
+
+
+# --------------------------------------------------------------------------
+# Per-output-channel weight scales (one fp32 scale per row of W)
+# --------------------------------------------------------------------------
+
+def _rowscaled(wb: np.ndarray, seed: int, span: int = 12) -> np.ndarray:
+    """The weight with row r scaled by 2^e_r, e_r uniform in [-span, span]
+    (exact in bf16 away from the subnormal range): row magnitudes that one
+    per-tensor scale cannot serve, like the fused Q, K and V blocks."""
+    e = np.random.default_rng(seed).integers(-span, span + 1, wb.shape[0])
+    w = oracle.bf16_to_f64(wb) * 2.0 ** e[:, None]
+    return synth.f32_to_bf16_bits(w.astype(np.float32))
+
+
+def _dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_per_channel_quantize_and_dequant_bitexact(layer, g):
+    _announce(f"per-channel quantize+dequant {layer.name} g={g}")
+    wb = _rowscaled(layer.w(), layer.n)
+    wq, s_w = cr.convrot_quantize_weights_per_channel(dev_bf16(wb), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights_per_channel(wb, g, SEED)
+    assert np.array_equal(f32_bits(s_w.cpu().numpy()), f32_bits(s_ref))
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    w_hat = host_bits(cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED))
+    assert np.array_equal(w_hat, oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+    ref = oracle.dequant_reference_f64(wq_ref, s_ref, g, SEED)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(w_hat), ref) < 1e-2
+    # every row on its own scale: the smallest rows are as accurate as the largest
+    w = oracle.bf16_to_f64(wb)
+    row_err = np.linalg.norm(oracle.bf16_to_f64(w_hat) - w, axis=1) / np.linalg.norm(w, axis=1)
+    assert row_err.max() < 0.05
+
+
+@pytest.mark.parametrize("g", GS)
+def test_per_channel_edge_weights(g):
+    _announce(f"per-channel edge weights g={g}")
+    for wb in (_edge_rows(256), _edge_rows(3072), np.zeros((16, 256), dtype=np.uint16)):
+        wq, s_w = cr.convrot_quantize_weights_per_channel(dev_bf16(wb), g, SEED)
+        wq_ref, s_ref = oracle.quantize_weights_per_channel(wb, g, SEED)
+        assert np.array_equal(f32_bits(s_w.cpu().numpy()), f32_bits(s_ref))
+        assert np.array_equal(wq.cpu().numpy(), wq_ref)
+        w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
+        assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+
+
+@pytest.mark.parametrize("g", (16, 64, 256))
+def test_per_channel_square_weight_decodes_rows_not_columns(g):
+    """out == in: scales applied along the wrong axis would still run; the
+    decode must return every row's impulse exactly."""
+    _announce(f"per-channel square impulses g={g}")
+    k = 256
+    w = np.zeros((k, k), dtype=np.float32)
+    for r in range(k):
+        w[r, (37 * r) % k] = (-1.0) ** r * 2.0 ** ((r % 29) - 14)
+    wb = synth.f32_to_bf16_bits(w)
+    wq, s_w = cr.convrot_quantize_weights_per_channel(dev_bf16(wb), g, SEED)
+    w_hat = host_bits(cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED))
+    assert np.array_equal(oracle.bf16_to_f64(w_hat), w.astype(np.float64))
+
+
+@pytest.mark.parametrize("tile", [0, 128, 192, 256])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (255, 16, 192), (257, 272, 320), (33, 1040, 64),
+                                   (400, 592, 384), (300, 400, 1152), (300, 400, 1088)])
+def test_per_channel_gemm_shapes(m, n, k, tile):
+    _announce(f"per-channel gemm shape {m}x{n}x{k} tile={tile}")
+    rng = np.random.default_rng(m * 5 + n)
+    xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    wq = rng.integers(-127, 128, (n, k)).astype(np.int8)
+    sx = (rng.random(m) * 1e-3).astype(np.float32)
+    sw = (rng.random(n) * 2.0 ** rng.integers(-20, 0, n)).astype(np.float32)
+    bias = synth.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    for b in (None, bias):
+        y, acc = cr.convrot_gemm_int8_per_channel(
+            torch.from_numpy(xq).to(DEV), _dev_f32(sx), torch.from_numpy(wq).to(DEV),
+            _dev_f32(sw), None if b is None else dev_bf16(b), want_acc=True, tile=tile)
+        acc_ref = oracle.gemm_int32(xq, wq)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert np.array_equal(host_bits(y), oracle.epilogue(acc_ref, sw, sx, b))
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_per_channel_linear_bitexact_and_tolerances(layer, g):
+    _announce(f"per-channel linear {layer.name} g={g}")
+    xb = layer.x()
+    wb = _rowscaled(layer.w(), layer.n + 1)
+    wq_ref, s_ref = oracle.quantize_weights_per_channel(wb, g, SEED)
+    bias_b = synth.f32_to_bf16_bits(
+        np.random.default_rng(8).standard_normal(layer.n).astype(np.float32))
+    y_ref, _, sx_ref, acc_ref = oracle.linear_int8(xb, wq_ref, s_ref, g, SEED, bias_b)
+    x = dev_bf16(xb)
+    wq = torch.from_numpy(wq_ref).to(DEV)
+    s_w = _dev_f32(s_ref)
+    got = host_bits(cr.convrot_linear_int8_per_channel(x, wq, s_w, g, SEED, dev_bf16(bias_b)))
+    assert np.array_equal(got, y_ref)
+    ref = oracle.linear_int8_reference_f64(acc_ref, s_ref, sx_ref, bias_b)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(got), ref) < 1e-2
+    # slicing invariance with per-channel scales
+    ws = torch.empty(cr.convrot_linear_int8_workspace_for_rows(37, layer.k), dtype=torch.uint8,
+                     device=DEV)
+    sliced = cr.convrot_linear_int8_per_channel(x, wq, s_w, g, SEED, dev_bf16(bias_b),
+                                                workspace=ws)
+    assert np.array_equal(host_bits(sliced), y_ref)
+    # the default path with per-channel scales, consumed by a bf16 matmul
+    w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
+    y_deq = (x.float() @ w_hat.float().t()).to(torch.bfloat16)
+    ref_deq = oracle.dequant_linear_reference_f64(xb, wq_ref, s_ref, g, SEED)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
+
+
+def test_per_channel_with_constant_scales_equals_per_tensor():
+    """a per-channel vector holding one value reproduces the per-tensor calls"""
+    _announce("per-channel constant scales")
+    layer, g = synth.ZIMAGE_ATTN.scaled(m=300, n=272), 256
+    wq, s_t = cr.convrot_quantize_weights(dev_bf16(layer.w()), g, SEED)
+    s_vec = s_t.expand(layer.n).contiguous()
+    x = dev_bf16(layer.x())
+    assert torch.equal(cr.convrot_linear_int8_per_channel(x, wq, s_vec, g, SEED),
+                       cr.convrot_linear_int8(x, wq, s_t, g, SEED))
+    assert torch.equal(cr.convrot_dequant_derotate_per_channel(wq, s_vec, g, SEED),
+                       cr.convrot_dequant_derotate(wq, s_t, g, SEED))
+
+
+def test_per_channel_binding_rejects_wrong_scale_length():
+    wq = torch.zeros((32, 256), dtype=torch.int8, device=DEV)
+    with pytest.raises(ValueError):
+        cr.convrot_dequant_derotate_per_channel(wq, torch.ones(31, device=DEV), 256)
+    with pytest.raises(cr.ConvrotError) as e:     # 4-byte aligned only
+        buf = torch.ones(40, device=DEV)
+        cr.convrot_dequant_derotate_per_channel(wq, buf[1:33], 256)
+    assert e.value.status_name == "CONVROT_E_MISALIGNED"

@@ -40,6 +40,11 @@ What the pages leave open, and the reading taken here
   commit list): s_w[n] = RN(amax_n/127) over row n of the rotated weight,
   the row quantized with it as a token row is; dequant uses RN(s_w[n]*2^-k)
   for row n; the epilogue uses s_w[n] for output column n.
+* FP16 (the pages' kernels run in BF16 and FP16: Invoke docs "int8 Compute",
+  the table of layers that keep unpacking): x, bias, y and W_hat may be
+  IEEE half instead of bf16. Every step is the same; only the decoding of the
+  inputs and the final rounding (RN to half, ties to even, overflow to inf)
+  change.
 
 Arithmetic is float64 (exact where the text says so) or exact integers.
 """
@@ -128,6 +133,38 @@ def f32_to_bf16(a: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
 
 
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE half bit patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def f32_to_f16(a: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE half bits, round to nearest, ties to even; magnitudes
+    from 65520 up become inf (IEEE 754 overflow under that rounding)."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+# decode, encode and significand fraction bits of each 16-bit format
+_FORMATS = {"bf16": (bf16_to_f64, f32_to_bf16, 7), "f16": (f16_to_f64, f32_to_f16, 10)}
+
+
+def _fmt(dtype: str):
+    if dtype not in _FORMATS:
+        raise ValueError(f"dtype must be one of {sorted(_FORMATS)}")
+    return _FORMATS[dtype]
+
+
+def to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """16-bit patterns of `dtype` -> float64 (exact)."""
+    return _fmt(dtype)[0](bits)
+
+
+def from_f32(a: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """float32 -> 16-bit patterns of `dtype`, round to nearest even."""
+    return _fmt(dtype)[1](a)
+
+
 def round_exact_to_f32(n: int, e: int) -> np.float32:
     """The float32 nearest to the exact value n * 2^e (ties to even),
     including the subnormal range. n, e are Python integers."""
@@ -158,13 +195,13 @@ def round_exact_to_f32(n: int, e: int) -> np.float32:
 # Rotation of rows: exact sum, rounded once to fp32
 # ----------------------------------------------------------------------------
 
-def _group_exponent_span_ok(v: np.ndarray, g: int) -> np.ndarray:
+def _group_exponent_span_ok(v: np.ndarray, g: int, frac_bits: int = 7) -> np.ndarray:
     """Per group (rows of v, shape [G, g]): True when every partial sum of
     +-v[i]*2^-k is exactly representable in float64, so any summation order
-    gives the exact sum. With 2^e <= |v| < 2^(e+1) and bf16's 8-bit
-    significand, every term is a multiple of 2^(e_min-7-k) and every partial
-    sum is below g*2^(e_max+1-k); 53 bits cover that when
-    e_max - e_min <= 45 - log2(g)."""
+    gives the exact sum. With 2^e <= |v| < 2^(e+1) and frac_bits fraction
+    bits (7 for bf16, 10 for half), every term is a multiple of
+    2^(e_min-frac_bits-k) and every partial sum is below g*2^(e_max+1-k); 53
+    bits cover that when e_max - e_min <= 52 - frac_bits - log2(g)."""
     a = np.abs(v)
     nz = a > 0
     _, ex = np.frexp(np.where(nz, a, 1.0))
@@ -172,13 +209,13 @@ def _group_exponent_span_ok(v: np.ndarray, g: int) -> np.ndarray:
     emax = np.where(nz, e, -(1 << 30)).max(axis=1)
     emin = np.where(nz, e, 1 << 30).min(axis=1)
     allzero = ~nz.any(axis=1)
-    return allzero | (emax - emin <= 45 - int(math.log2(g)))
+    return allzero | (emax - emin <= 52 - frac_bits - int(math.log2(g)))
 
 
-def _rotate_groups_exact_int(v: np.ndarray, g: int, seed: int) -> np.ndarray:
-    """Exact route for groups [G, g] (float64 holding bf16 values): scale each
-    group to integers, form the signed sums with integer arithmetic, round
-    each sum once to float32."""
+def _rotate_groups_exact_int(v: np.ndarray, g: int, seed: int, frac_bits: int = 7) -> np.ndarray:
+    """Exact route for groups [G, g] (float64 holding 16-bit float values with
+    frac_bits fraction bits): scale each group to integers, form the signed
+    sums with integer arithmetic, round each sum once to float32."""
     h = hadamard(g)
     d = rotation_signs(seed, g)
     k = int(math.log2(math.isqrt(g)))      # 1/sqrt(g) = 2^-k
@@ -191,7 +228,7 @@ def _rotate_groups_exact_int(v: np.ndarray, g: int, seed: int) -> np.ndarray:
             out[r] = 0.0
             continue
         _, ex = np.frexp(np.abs(row[nz]))
-        s = 7 - (int(ex.min()) - 1)        # every value is a multiple of 2^-s
+        s = frac_bits - (int(ex.min()) - 1)   # every value is a multiple of 2^-s
         xs = [int(math.ldexp(float(t), s)) for t in row]   # exact integers
         # signed sums y_j = sum_i H[i, j] * xs[i], in 40-bit limbs so that a
         # plain int64 matmul is exact (|partial| < g * 2^40 < 2^63)
@@ -211,27 +248,29 @@ def _rotate_groups_exact_int(v: np.ndarray, g: int, seed: int) -> np.ndarray:
 
 
 def rotate_rows(x_bits: np.ndarray, g: int, seed: int, *, force_exact: bool = False,
-                return_flag_count: bool = False):
+                return_flag_count: bool = False, dtype: str = "bf16"):
     """x_r = x . blockdiag(R) per g-group of the last axis, each element the
     exact sum rounded once to float32.
 
-    x_bits: bf16 bit patterns [rows, K] with K % g == 0.
+    x_bits: bf16 (or, with dtype="f16", half) bit patterns [rows, K], K % g == 0.
     Groups whose exponent span keeps every float64 partial sum exact use a
     dense float64 block matmul [rows*K/g, g] @ R; the rest (and all groups
     when force_exact) use exact integer sums.
     """
-    x = bf16_to_f64(x_bits)
+    decode, _, frac_bits = _fmt(dtype)
+    x = decode(x_bits)
     rows, kdim = x.shape
     if kdim % g:
         raise ValueError("K must be a multiple of g")
     v = x.reshape(-1, g)
-    ok = np.zeros(v.shape[0], dtype=bool) if force_exact else _group_exponent_span_ok(v, g)
+    ok = np.zeros(v.shape[0], dtype=bool) if force_exact else \
+        _group_exponent_span_ok(v, g, frac_bits)
     out = np.empty(v.shape, dtype=np.float32)
     if ok.any():
         out[ok] = (v[ok] @ rotation_matrix(g, seed)).astype(np.float32)
     bad = ~ok
     if bad.any():
-        out[bad] = _rotate_groups_exact_int(v[bad], g, seed)
+        out[bad] = _rotate_groups_exact_int(v[bad], g, seed, frac_bits)
     out = out.reshape(rows, kdim)
     if return_flag_count:
         return out, int(bad.sum())
@@ -264,10 +303,10 @@ def quantize_with_amax(v: np.ndarray, amax: np.ndarray):
     return q, s
 
 
-def quantize_activations(x_bits: np.ndarray, g: int, seed: int):
-    """Per-token (per-row) rotate + absmax + int8 quantize.
+def quantize_activations(x_bits: np.ndarray, g: int, seed: int, dtype: str = "bf16"):
+    """Per-token (per-row) rotate + absmax + int8 quantize of x (bf16 or half).
     Returns xq int8 [M, K], s_x float32 [M]."""
-    xr = rotate_rows(x_bits, g, seed)
+    xr = rotate_rows(x_bits, g, seed, dtype=dtype)
     amax = np.abs(xr).max(axis=1) if xr.shape[1] else np.zeros(xr.shape[0], np.float32)
     return quantize_with_amax(xr, amax.astype(np.float32))
 
@@ -314,13 +353,14 @@ def derotation_integers(wq: np.ndarray, g: int, seed: int) -> np.ndarray:
     return (grp @ h).reshape(n, kdim)
 
 
-def dequant_derotate(wq: np.ndarray, s_w, g: int, seed: int) -> np.ndarray:
+def dequant_derotate(wq: np.ndarray, s_w, g: int, seed: int, out_dtype: str = "bf16") -> np.ndarray:
     """W_hat (bf16 bits) = RN_bf16(RN32(float(S) * c)), c = RN32(s_w*2^-k);
-    with a per-channel s_w [N], row n uses c_n = RN32(s_w[n]*2^-k)."""
+    with a per-channel s_w [N], row n uses c_n = RN32(s_w[n]*2^-k).
+    out_dtype="f16" rounds to half instead."""
     k = int(math.log2(math.isqrt(g)))
     c = (_row_scales(s_w, wq.shape[0]) * np.float32(2.0 ** -k)).astype(np.float32)
     s_int = derotation_integers(wq, g, seed)
-    return f32_to_bf16((s_int.astype(np.float32) * c[:, None]).astype(np.float32))
+    return from_f32((s_int.astype(np.float32) * c[:, None]).astype(np.float32), out_dtype)
 
 
 def dequant_reference_f64(wq: np.ndarray, s_w, g: int, seed: int) -> np.ndarray:
@@ -348,44 +388,48 @@ def gemm_int32(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
     return acc.astype(np.int64).astype(np.int32)
 
 
-def epilogue(acc: np.ndarray, s_w, s_x: np.ndarray, bias_bits: np.ndarray | None = None):
+def epilogue(acc: np.ndarray, s_w, s_x: np.ndarray, bias_bits: np.ndarray | None = None,
+             dtype: str = "bf16"):
     """y = RN_bf16(RN32(RN32(float(acc) * s_w) * s_x[m]) [+ bias[n]]) -> bf16 bits;
-    a per-channel s_w [N] scales output column n."""
+    a per-channel s_w [N] scales output column n. dtype="f16": bias and y are
+    half (y rounded once from the same fp32 value)."""
     t = acc.astype(np.float32)
     t = (t * _row_scales(s_w, acc.shape[1])[None, :]).astype(np.float32)
     t = (t * np.asarray(s_x, dtype=np.float32)[:, None]).astype(np.float32)
     if bias_bits is not None:
-        t = (t + bf16_to_f64(bias_bits).astype(np.float32)[None, :]).astype(np.float32)
-    return f32_to_bf16(t)
+        t = (t + to_f64(bias_bits, dtype).astype(np.float32)[None, :]).astype(np.float32)
+    return from_f32(t, dtype)
 
 
 def linear_int8(x_bits: np.ndarray, wq: np.ndarray, s_w, g: int, seed: int,
-                bias_bits: np.ndarray | None = None):
+                bias_bits: np.ndarray | None = None, dtype: str = "bf16"):
     """The int8_compute forward: rotate + quantize x per token, int8 GEMM,
-    scale epilogue. Returns (y bf16 bits, xq, s_x, acc)."""
-    xq, s_x = quantize_activations(x_bits, g, seed)
+    scale epilogue; x, bias and y in `dtype`. Returns (y bits, xq, s_x, acc)."""
+    xq, s_x = quantize_activations(x_bits, g, seed, dtype)
     acc = gemm_int32(xq, wq)
-    return epilogue(acc, s_w, s_x, bias_bits), xq, s_x, acc
+    return epilogue(acc, s_w, s_x, bias_bits, dtype), xq, s_x, acc
 
 
 def linear_int8_reference_f64(acc: np.ndarray, s_w, s_x: np.ndarray,
-                              bias_bits: np.ndarray | None = None) -> np.ndarray:
+                              bias_bits: np.ndarray | None = None,
+                              dtype: str = "bf16") -> np.ndarray:
     """s_w * s_x[m] * acc (+ bias) in float64: the tolerance reference of the
     int8_compute output."""
     sw = _row_scales(s_w, acc.shape[1]).astype(np.float64)
     y = sw[None, :] * np.asarray(s_x, dtype=np.float64)[:, None] * acc.astype(np.float64)
     if bias_bits is not None:
-        y = y + bf16_to_f64(bias_bits)[None, :]
+        y = y + to_f64(bias_bits, dtype)[None, :]
     return y
 
 
 def dequant_linear_reference_f64(x_bits: np.ndarray, wq: np.ndarray, s_w, g: int, seed: int,
-                                 bias_bits: np.ndarray | None = None) -> np.ndarray:
+                                 bias_bits: np.ndarray | None = None,
+                                 dtype: str = "bf16") -> np.ndarray:
     """x . (s_w Wq blockdiag(R)^T)^T in float64: the tolerance reference of the
     default (dequant) path."""
-    y = bf16_to_f64(x_bits) @ dequant_reference_f64(wq, s_w, g, seed).T
+    y = to_f64(x_bits, dtype) @ dequant_reference_f64(wq, s_w, g, seed).T
     if bias_bits is not None:
-        y = y + bf16_to_f64(bias_bits)[None, :]
+        y = y + to_f64(bias_bits, dtype)[None, :]
     return y
 
 

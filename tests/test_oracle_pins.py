@@ -514,3 +514,123 @@ def test_linear_int8_per_channel_tolerances():
     yt = o.bf16_to_f64(o.linear_int8(xb, wq_t, s_t, 256, SEED)[0])
     col_err_t = np.linalg.norm(yt - true, axis=0) / np.linalg.norm(true, axis=0)
     assert col_err_t.max() > 0.5
+
+
+# --------------------------------------------------------------------------
+# FP16 activations and outputs (the pages' kernels run in BF16 and FP16:
+# Invoke docs "int8 Compute", the table of layers that keep unpacking)
+# --------------------------------------------------------------------------
+
+def test_f32_to_f16_known_values_and_torch():
+    """IEEE 754 half, round to nearest even: printed bit patterns of the
+    binary16 format, then agreement with torch's own conversion"""
+    cases = [(1.0, 0x3C00), (-2.5, 0xC100), (65504.0, 0x7BFF), (65519.99, 0x7BFF),
+             (65520.0, 0x7C00), (-1e6, 0xFC00), (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000),
+             (3 * 2.0 ** -26, 0x0001), (1 + 2.0 ** -11, 0x3C00), (1 + 3 * 2.0 ** -11, 0x3C02),
+             (2.0 ** -14, 0x0400), (0.0, 0x0000), (-0.0, 0x8000)]
+    got = o.f32_to_f16(np.array([c for c, _ in cases], dtype=np.float32))
+    assert [int(v) for v in got] == [b for _, b in cases]
+    rng = np.random.default_rng(40)
+    a = (rng.standard_normal(200000) * 2.0 ** rng.integers(-30, 17, 200000)).astype(np.float32)
+    want = torch.from_numpy(a).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.f32_to_f16(a), want)
+    # decode is exact
+    bits = np.arange(0, 0x7C00, 7, dtype=np.uint16)
+    assert np.array_equal(o.f16_to_f64(bits), bits.view(np.float16).astype(np.float64))
+
+
+def _f16_groups(rng, rows, k):
+    """half values with the widest spans the format allows: subnormals
+    (multiples of 2^-24) beside values near 65504"""
+    x = rng.standard_normal((rows, k)) * 2.0 ** rng.integers(-26, 16, (rows, k))
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    x[:, ::17] = np.float16(2.0 ** -24)
+    x[:, 5::19] = np.float16(-65504.0)
+    return x.view(np.uint16)
+
+
+@pytest.mark.parametrize("g", GS)
+def test_f16_float64_transform_is_exact(g):
+    """Every half value is a multiple of 2^-24 below 2^16, so the signed sums
+    of a group are multiples of 2^-24 below 2^24: any float64 summation is
+    exact. Checked against exact integer sums on the widest spans."""
+    rng = np.random.default_rng(41 + g)
+    xb = _f16_groups(rng, 6, 512)
+    fast = o.rotate_rows(xb, g, SEED, dtype="f16")
+    exact = o.rotate_rows(xb, g, SEED, dtype="f16", force_exact=True)
+    assert np.array_equal(fast.view(np.uint32), exact.view(np.uint32))
+    # and a float64 sum in another order (reversed terms) lands on the same values
+    x = o.f16_to_f64(xb).reshape(-1, g)
+    r = o.rotation_matrix(g, SEED)
+    rev = (x[:, ::-1] @ r[::-1, :]).astype(np.float32).reshape(fast.shape)
+    assert np.array_equal(rev.view(np.uint32), fast.view(np.uint32))
+
+
+def test_f16_exact_route_uses_half_significand():
+    """the integer route on half values that need all 11 significant bits"""
+    g = 16
+    x = np.zeros((1, g), dtype=np.float16)
+    for tiny in (2.0 ** -24, 1.5):                 # smallest element tiny, or not
+        x[0, 0] = np.float16(1 + 2.0 ** -10)       # 11 significant bits
+        x[0, 1] = np.float16(tiny)
+        xb = x.view(np.uint16)
+        got = o.rotate_rows(xb, g, SEED, dtype="f16", force_exact=True)
+        d = o.rotation_signs(SEED, g)
+        h = o.hadamard(g)
+        want = np.array([float(Fraction(1 + 2.0 ** -10) * int(h[0, j]) + Fraction(tiny)
+                               * int(h[1, j])) * int(d[j]) / 4 for j in range(g)],
+                        dtype=np.float32)
+        assert np.array_equal(got[0], want), tiny
+
+
+def test_f16_and_bf16_agree_where_both_hold_x():
+    """values with at most 8 significant bits inside half's normal range are
+    the same numbers in both formats: identical codes and scales"""
+    rng = np.random.default_rng(42)
+    v = rng.standard_normal((16, 512)) * 2.0 ** rng.integers(-10, 10, (16, 512))
+    v = o.bf16_to_f64(synth.f32_to_bf16_bits(v.astype(np.float32)))
+    v = np.where(np.abs(v) < 2.0 ** -14, 0.0, v)
+    v = np.clip(v, -60000, 60000)
+    bb = synth.f32_to_bf16_bits(v.astype(np.float32))
+    hb = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(o.f16_to_f64(hb), o.bf16_to_f64(bb))
+    for g in GS:
+        q1, s1 = o.quantize_activations(bb, g, SEED)
+        q2, s2 = o.quantize_activations(hb, g, SEED, "f16")
+        assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
+def test_f16_epilogue_closed_form_and_overflow():
+    acc = np.array([[1, -1, 1000, 70000, 65504, 65520]], dtype=np.int32)
+    s_x = np.array([1.0], dtype=np.float32)
+    y = o.epilogue(acc, np.float32(1.0), s_x, dtype="f16")
+    assert [int(t) for t in y[0]] == [0x3C00, 0xBC00, 0x63D0, 0x7C00, 0x7BFF, 0x7C00]
+    bias = np.array([0x3C00] * 6, dtype=np.uint16)          # +1.0 in half
+    yb = o.epilogue(acc, np.float32(1.0), s_x, bias, dtype="f16")
+    assert int(yb[0, 0]) == 0x4000 and int(yb[0, 1]) == 0x0000
+    # bf16 bias bits read as bf16 would give a different value: the dtype decides
+    assert o.f16_to_f64(np.array([0x3C00], np.uint16))[0] == 1.0
+    assert o.bf16_to_f64(np.array([0x3C00], np.uint16))[0] == 2.0 ** -7
+
+
+@pytest.mark.parametrize("g", GS)
+def test_f16_dequant_recovers_impulses(g):
+    k = 256
+    w = np.zeros((2, k), dtype=np.float32)
+    w[0, 0] = 1.0
+    w[1, 3] = -1.0
+    wq, s_w = o.quantize_weights(synth.f32_to_bf16_bits(w), g, SEED)
+    w_hat = o.f16_to_f64(o.dequant_derotate(wq, s_w, g, SEED, "f16"))
+    assert np.array_equal(w_hat, w.astype(np.float64))
+
+
+def test_f16_linear_tolerances():
+    layer = synth.TINY
+    xb = o.f32_to_f16(o.bf16_to_f64(layer.x()).astype(np.float32))
+    wq, s_w = o.quantize_weights(layer.w(), 256, SEED)
+    bias = o.f32_to_f16(np.random.default_rng(43).standard_normal(layer.n).astype(np.float32))
+    y, xq, sx, acc = o.linear_int8(xb, wq, s_w, 256, SEED, bias, "f16")
+    yf = o.f16_to_f64(y)
+    assert o.rel_frobenius(yf, o.linear_int8_reference_f64(acc, s_w, sx, bias, "f16")) < 2.0 ** -10
+    true = o.f16_to_f64(xb) @ o.bf16_to_f64(layer.w()).T + o.f16_to_f64(bias)[None, :]
+    assert o.rel_frobenius(yf, true) < 0.05

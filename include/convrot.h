@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 2
+#define CONVROT_ABI_VERSION 3
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -85,6 +85,22 @@ typedef enum convrot_status {
   CONVROT_E_WORKSPACE = 5,         /* workspace too small for one token row                   */
   CONVROT_E_HIP = 6                /* a HIP call failed; see convrot_last_error_string()      */
 } convrot_status;
+
+/* 16-bit float format of activations, bias, outputs and W_hat (the *_ex
+ * entry points). The pages' kernels run in BF16 and FP16 (Invoke docs "int8
+ * Compute", the table of layers that keep unpacking). With FP16 every step is
+ * the same; only the input decoding and the final rounding (to nearest even,
+ * overflow to inf) change. IEEE half inputs never need the exact kernel:
+ * each value is a multiple of 2^-24 below 2^16, so the float64 transform of a
+ * group is exact. Non-finite inputs are out of contract for both formats. */
+typedef enum convrot_dtype { CONVROT_DTYPE_BF16 = 0, CONVROT_DTYPE_F16 = 1 } convrot_dtype;
+
+/* Weight scale granularity (the *_ex entry points): one fp32 for the tensor,
+ * or one per output channel (n fp32, 16-byte aligned; see above). */
+typedef enum convrot_scale_mode {
+  CONVROT_SCALE_PER_TENSOR = 0,
+  CONVROT_SCALE_PER_CHANNEL = 1
+} convrot_scale_mode;
 
 /* Rotate, absmax and quantize a weight to int8 with one scale per tensor.
  *   w   [n, k] bf16 (in)     the unquantized weight (out features x in features)
@@ -186,6 +202,32 @@ convrot_status convrot_linear_int8_per_channel(const uint16_t* x, const int8_t* 
                                                int64_t n, int64_t k, int g, uint64_t rot_seed,
                                                uint16_t* y, void* workspace,
                                                size_t workspace_bytes, void* stream);
+
+/* General forms: every combination of activation format (dtype) and weight
+ * scale granularity (scale_mode). x, bias, y and w_out are 16-bit tensors of
+ * the given format; everything else is as in the entry points above, and an
+ * unknown dtype or scale_mode value is CONVROT_E_INVALID_ARG.
+ *   convrot_quantize_activations_ex: x [m, k] -> xq [m, k] int8, s_x [m]
+ *   convrot_dequant_derotate_ex:     wq [n, k], s_w -> w_out [n, k] in out_dtype
+ *   convrot_gemm_int8_ex:            y (nullable) in dtype, acc (nullable);
+ *                                    tile 0 = automatic, else 128/192/256
+ *   convrot_linear_int8_ex:          x, bias, y in dtype; same workspace rules */
+convrot_status convrot_quantize_activations_ex(const void* x, convrot_dtype dtype, int64_t m,
+                                               int64_t k, int g, uint64_t rot_seed, int8_t* xq,
+                                               float* s_x, void* stream);
+convrot_status convrot_dequant_derotate_ex(const int8_t* wq, const float* s_w,
+                                           convrot_scale_mode scale_mode, int64_t n, int64_t k,
+                                           int g, uint64_t rot_seed, void* w_out,
+                                           convrot_dtype out_dtype, void* stream);
+convrot_status convrot_gemm_int8_ex(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                    const float* s_w, convrot_scale_mode scale_mode,
+                                    const void* bias, int64_t m, int64_t n, int64_t k, void* y,
+                                    int32_t* acc, convrot_dtype dtype, int tile, void* stream);
+convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const float* s_w,
+                                      convrot_scale_mode scale_mode, const void* bias, int64_t m,
+                                      int64_t n, int64_t k, int g, uint64_t rot_seed, void* y,
+                                      convrot_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);

@@ -23,7 +23,8 @@ __all__ = [
     "convrot_rotation_signs", "convrot_abi_version", "convrot_status_string",
     "convrot_quantize_weights_per_channel", "convrot_dequant_derotate_per_channel",
     "convrot_gemm_int8_per_channel", "convrot_linear_int8_per_channel",
-    "EXPORTED_SYMBOLS",
+    "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
+    "convrot_linear_int8_ex", "EXPORTED_SYMBOLS",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -42,7 +43,13 @@ EXPORTED_SYMBOLS = (
     "convrot_quantize_weights_per_channel", "convrot_dequant_derotate_per_channel",
     "convrot_gemm_int8_per_channel", "convrot_gemm_int8_per_channel_tile",
     "convrot_linear_int8_per_channel",
+    "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
+    "convrot_linear_int8_ex",
 )
+
+# convrot_dtype and convrot_scale_mode values
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+_SCALE_PER_TENSOR, _SCALE_PER_CHANNEL = 0, 1
 
 _STATUS = {0: "CONVROT_OK", 1: "CONVROT_E_INVALID_ARG", 2: "CONVROT_E_UNSUPPORTED_GROUP",
            3: "CONVROT_E_UNSUPPORTED_SHAPE", 4: "CONVROT_E_MISALIGNED", 5: "CONVROT_E_WORKSPACE",
@@ -89,6 +96,10 @@ def load_library():
             "convrot_gemm_int8_per_channel": [P, P, P, P, P, I64, I64, I64, P, P, P],
             "convrot_gemm_int8_per_channel_tile": [P, P, P, P, P, I64, I64, I64, P, P, I, P],
             "convrot_linear_int8_per_channel": [P, P, P, P, I64, I64, I64, I, U64, P, P, SZ, P],
+            "convrot_quantize_activations_ex": [P, I, I64, I64, I, U64, P, P, P],
+            "convrot_dequant_derotate_ex": [P, P, I, I64, I64, I, U64, P, I, P],
+            "convrot_gemm_int8_ex": [P, P, P, P, I, P, I64, I64, I64, P, P, I, I, P],
+            "convrot_linear_int8_ex": [P, P, P, I, P, I64, I64, I64, I, U64, P, I, P, SZ, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -335,3 +346,110 @@ def convrot_linear_int8_per_channel(x: torch.Tensor, wq: torch.Tensor, s_w: torc
     """convrot_linear_int8 with per-channel weight scales s_w fp32 [n]."""
     return _linear("convrot_linear_int8_per_channel", True, x, wq, s_w, g, rot_seed, bias,
                    workspace, out)
+
+
+# ---------------------------------------------------------------------------
+# General forms: bf16 or fp16 activations / outputs, per-tensor or per-channel
+# weight scales
+# ---------------------------------------------------------------------------
+
+def _need16(t: torch.Tensor, name: str, ndim: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor) or t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be a bfloat16 or float16 tensor")
+    _need(t, name, t.dtype, ndim)
+    return _DTYPES[t.dtype]
+
+
+def convrot_quantize_activations_ex(x: torch.Tensor, g: int, rot_seed: int = ROT_SEED, *,
+                                    xq: torch.Tensor | None = None,
+                                    s_x: torch.Tensor | None = None):
+    """x bf16 or fp16 [m, k] -> (xq int8 [m, k], s_x fp32 [m])."""
+    dt = _need16(x, "x", 2)
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device) if xq is None else xq
+    s_x = torch.empty(m, dtype=torch.float32, device=x.device) if s_x is None else s_x
+    _need(xq, "xq", torch.int8, 2)
+    _need(s_x, "s_x", torch.float32, 1)
+    _same_device(x, xq, s_x)
+    _check(load_library().convrot_quantize_activations_ex(_ptr(x), dt, m, k, g, rot_seed,
+                                                          _ptr(xq), _ptr(s_x), _stream(x)))
+    return xq, s_x
+
+
+def convrot_dequant_derotate_ex(wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                                rot_seed: int = ROT_SEED, *, per_channel: bool = False,
+                                out_dtype: torch.dtype = torch.bfloat16,
+                                out: torch.Tensor | None = None):
+    """Wq int8 [n, k], s_w fp32 [1] or [n] -> W_hat [n, k] in out_dtype (bf16 or fp16)."""
+    _need(wq, "wq", torch.int8, 2)
+    n, k = wq.shape
+    _need_sw(s_w, per_channel, n)
+    out = torch.empty((n, k), dtype=out_dtype, device=wq.device) if out is None else out
+    dt = _need16(out, "out", 2)
+    _same_device(wq, s_w, out)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_dequant_derotate_ex(_ptr(wq), _ptr(s_w), mode, n, k, g,
+                                                      rot_seed, _ptr(out), dt, _stream(wq)))
+    return out
+
+
+def convrot_gemm_int8_ex(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor,
+                         s_w: torch.Tensor, bias: torch.Tensor | None = None, *,
+                         per_channel: bool = False, dtype: torch.dtype = torch.bfloat16,
+                         want_y: bool = True, want_acc: bool = False,
+                         y: torch.Tensor | None = None, acc: torch.Tensor | None = None,
+                         tile: int = 0):
+    """int8 GEMM + epilogue with bias and y in `dtype` (bf16 or fp16)."""
+    if dtype not in _DTYPES:
+        raise TypeError("dtype must be torch.bfloat16 or torch.float16")
+    _need(xq, "xq", torch.int8, 2)
+    _need(wq, "wq", torch.int8, 2)
+    _need(s_x, "s_x", torch.float32, 1)
+    m, k = xq.shape
+    n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
+    if wq.shape[1] != k:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
+    if bias is not None:
+        _need(bias, "bias", dtype, 1)
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=dtype, device=xq.device)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    if y is not None:
+        _need(y, "y", dtype, 2)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, 2)
+    _same_device(xq, s_x, wq, s_w, bias, y, acc)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_gemm_int8_ex(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), mode,
+                                               _ptr(bias), m, n, k, _ptr(y), _ptr(acc),
+                                               _DTYPES[dtype], tile, _stream(xq)))
+    return y, acc
+
+
+def convrot_linear_int8_ex(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                           rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                           per_channel: bool = False, workspace: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None):
+    """The int8_compute forward in x's format (bf16 or fp16): bias and y too."""
+    dt = _need16(x, "x", 2)
+    _need(wq, "wq", torch.int8, 2)
+    m, k = x.shape
+    n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
+    if bias is not None:
+        _need(bias, "bias", x.dtype, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_int8_workspace_size(m, n, k), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    out = torch.empty((m, n), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out", x.dtype, 2)
+    _same_device(x, wq, s_w, bias, workspace, out)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_linear_int8_ex(_ptr(x), _ptr(wq), _ptr(s_w), mode, _ptr(bias),
+                                                 m, n, k, g, rot_seed, _ptr(out), dt,
+                                                 _ptr(workspace), workspace.numel(),
+                                                 _stream(x)))
+    return out

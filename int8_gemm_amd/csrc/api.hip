@@ -102,6 +102,18 @@ convrot_status check_gemm(const char* fn, int64_t m, int64_t n, int64_t k) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// enum arguments of the *_ex entry points
+bool dtype_of(int v, DType* dt) {
+  if (v != CONVROT_DTYPE_BF16 && v != CONVROT_DTYPE_F16) return false;
+  *dt = v == CONVROT_DTYPE_F16 ? DType::kF16 : DType::kBF16;
+  return true;
+}
+bool scale_mode_of(int v, bool* pc) {
+  if (v != CONVROT_SCALE_PER_TENSOR && v != CONVROT_SCALE_PER_CHANNEL) return false;
+  *pc = v == CONVROT_SCALE_PER_CHANNEL;
+  return true;
+}
+
 // Per-tensor s_w: one fp32, 4-byte aligned. Per-channel s_w: n fp32, 16-byte
 // aligned (the GEMM epilogue reads four consecutive scales at once).
 size_t sw_bytes(bool pc, int64_t n) { return pc ? (size_t)n * 4 : 4; }
@@ -152,7 +164,7 @@ static convrot_status quantize_weights_impl(const char* fn, bool pc, const uint1
   const SignMask sm = make_signs(rot_seed, g);
   // per channel, a weight row is quantized exactly as a token row is
   const hipError_t e =
-      pc ? launch_quantize_rows(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream)
+      pc ? launch_quantize_rows(w, wq, s_w, n, (int)k, g, sm, DType::kBF16, (hipStream_t)stream)
          : launch_quantize_tensor(w, wq, s_w, n, (int)k, g, sm, (hipStream_t)stream);
   return hip_status(e, fn);
 }
@@ -171,9 +183,9 @@ convrot_status convrot_quantize_weights_per_channel(const uint16_t* w, int64_t n
                                wq, s_w, stream);
 }
 
-static convrot_status dequant_impl(const char* fn, bool pc, const int8_t* wq, const float* s_w,
-                                   int64_t n, int64_t k, int g, uint64_t rot_seed,
-                                   uint16_t* w_out, void* stream) {
+static convrot_status dequant_impl(const char* fn, bool pc, DType dt, const int8_t* wq,
+                                   const float* s_w, int64_t n, int64_t k, int g,
+                                   uint64_t rot_seed, uint16_t* w_out, void* stream) {
   if (!wq || !s_w || !w_out) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
   if (convrot_status s = check_rot(fn, n, k, g)) return s;
@@ -183,26 +195,42 @@ static convrot_status dequant_impl(const char* fn, bool pc, const int8_t* wq, co
       overlap(s_w, sw_bytes(pc, n), w_out, (size_t)(n * k) * 2))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   const SignMask sm = make_signs(rot_seed, g);
-  return hip_status(launch_dequant(wq, s_w, pc, n, k, g, sm, w_out, (hipStream_t)stream), fn);
+  return hip_status(launch_dequant(wq, s_w, pc, n, k, g, sm, w_out, dt, (hipStream_t)stream),
+                    fn);
 }
 
 convrot_status convrot_dequant_derotate(const int8_t* wq, const float* s_w, int64_t n, int64_t k,
                                         int g, uint64_t rot_seed, uint16_t* w_out,
                                         void* stream) {
-  return dequant_impl("convrot_dequant_derotate", false, wq, s_w, n, k, g, rot_seed, w_out,
-                      stream);
+  return dequant_impl("convrot_dequant_derotate", false, DType::kBF16, wq, s_w, n, k, g, rot_seed,
+                      w_out, stream);
 }
 
 convrot_status convrot_dequant_derotate_per_channel(const int8_t* wq, const float* s_w, int64_t n,
                                                     int64_t k, int g, uint64_t rot_seed,
                                                     uint16_t* w_out, void* stream) {
-  return dequant_impl("convrot_dequant_derotate_per_channel", true, wq, s_w, n, k, g, rot_seed,
-                      w_out, stream);
+  return dequant_impl("convrot_dequant_derotate_per_channel", true, DType::kBF16, wq, s_w, n, k, g,
+                      rot_seed, w_out, stream);
 }
 
-static convrot_status quantize_activations_impl(const char* fn, bool exact, const uint16_t* x,
-                                                int64_t m, int64_t k, int g, uint64_t rot_seed,
-                                                int8_t* xq, float* s_x, void* stream) {
+convrot_status convrot_dequant_derotate_ex(const int8_t* wq, const float* s_w,
+                                           convrot_scale_mode scale_mode, int64_t n, int64_t k,
+                                           int g, uint64_t rot_seed, void* w_out,
+                                           convrot_dtype out_dtype, void* stream) {
+  const char* fn = "convrot_dequant_derotate_ex";
+  bool pc;
+  DType dt;
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(out_dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d out_dtype=%d", fn, (int)scale_mode,
+                (int)out_dtype);
+  return dequant_impl(fn, pc, dt, wq, s_w, n, k, g, rot_seed, static_cast<uint16_t*>(w_out),
+                      stream);
+}
+
+static convrot_status quantize_activations_impl(const char* fn, bool exact, DType dt,
+                                                const uint16_t* x, int64_t m, int64_t k, int g,
+                                                uint64_t rot_seed, int8_t* xq, float* s_x,
+                                                void* stream) {
   if (convrot_status s = check_rot(fn, m, k, g)) return s;
   if (m == 0) return ok();  // nothing to read or write; the M-sized buffers may be null
   if (!x || !xq || !s_x) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
@@ -216,25 +244,37 @@ static convrot_status quantize_activations_impl(const char* fn, bool exact, cons
   const SignMask sm = make_signs(rot_seed, g);
   hipError_t e = exact ? launch_quantize_rows_exact(x, xq, s_x, m, (int)k, g, sm,
                                                     (hipStream_t)stream)
-                       : launch_quantize_rows(x, xq, s_x, m, (int)k, g, sm, (hipStream_t)stream);
+                       : launch_quantize_rows(x, xq, s_x, m, (int)k, g, sm, dt,
+                                              (hipStream_t)stream);
   return hip_status(e, fn);
 }
 
 convrot_status convrot_quantize_activations(const uint16_t* x, int64_t m, int64_t k, int g,
                                             uint64_t rot_seed, int8_t* xq, float* s_x,
                                             void* stream) {
-  return quantize_activations_impl("convrot_quantize_activations", false, x, m, k, g, rot_seed,
-                                   xq, s_x, stream);
+  return quantize_activations_impl("convrot_quantize_activations", false, DType::kBF16, x, m, k,
+                                   g, rot_seed, xq, s_x, stream);
+}
+
+convrot_status convrot_quantize_activations_ex(const void* x, convrot_dtype dtype, int64_t m,
+                                               int64_t k, int g, uint64_t rot_seed, int8_t* xq,
+                                               float* s_x, void* stream) {
+  const char* fn = "convrot_quantize_activations_ex";
+  DType dt;
+  if (!dtype_of(dtype, &dt)) return fail(CONVROT_E_INVALID_ARG, "%s: dtype=%d", fn, (int)dtype);
+  return quantize_activations_impl(fn, false, dt, static_cast<const uint16_t*>(x), m, k, g,
+                                   rot_seed, xq, s_x, stream);
 }
 
 convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, int64_t k, int g,
                                                   uint64_t rot_seed, int8_t* xq, float* s_x,
                                                   void* stream) {
-  return quantize_activations_impl("convrot_quantize_activations_exact", true, x, m, k, g,
-                                   rot_seed, xq, s_x, stream);
+  return quantize_activations_impl("convrot_quantize_activations_exact", true, DType::kBF16, x, m,
+                                   k, g, rot_seed, xq, s_x, stream);
 }
 
-static convrot_status gemm_impl(const char* fn, bool pc, const int8_t* xq, const float* s_x,
+static convrot_status gemm_impl(const char* fn, bool pc, DType dt, const int8_t* xq,
+                                const float* s_x,
                                 const int8_t* wq, const float* s_w, const uint16_t* bias,
                                 int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc,
                                 int tile, void* stream) {
@@ -254,7 +294,7 @@ static convrot_status gemm_impl(const char* fn, bool pc, const int8_t* xq, const
       overlap(acc, na, s_w, sw_bytes(pc, n)))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
   if (m == 0) return ok();
-  return hip_status(launch_gemm_tile(xq, s_x, wq, s_w, pc, bias, m, n, k, y, acc, tile,
+  return hip_status(launch_gemm_tile(xq, s_x, wq, s_w, pc, bias, m, n, k, y, acc, tile, dt,
                                      (hipStream_t)stream),
                     fn);
 }
@@ -262,7 +302,7 @@ static convrot_status gemm_impl(const char* fn, bool pc, const int8_t* xq, const
 convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_t* wq,
                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
                                  int64_t k, uint16_t* y, int32_t* acc, void* stream) {
-  return gemm_impl("convrot_gemm_int8", false, xq, s_x, wq, s_w, bias, m, n, k, y, acc, 0,
+  return gemm_impl("convrot_gemm_int8", false, DType::kBF16, xq, s_x, wq, s_w, bias, m, n, k, y, acc, 0,
                    stream);
 }
 
@@ -271,7 +311,7 @@ convrot_status convrot_gemm_int8_per_channel(const int8_t* xq, const float* s_x,
                                              const uint16_t* bias, int64_t m, int64_t n,
                                              int64_t k, uint16_t* y, int32_t* acc,
                                              void* stream) {
-  return gemm_impl("convrot_gemm_int8_per_channel", true, xq, s_x, wq, s_w, bias, m, n, k, y, acc,
+  return gemm_impl("convrot_gemm_int8_per_channel", true, DType::kBF16, xq, s_x, wq, s_w, bias, m, n, k, y, acc,
                    0, stream);
 }
 
@@ -279,7 +319,7 @@ convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const 
                                       const float* s_w, const uint16_t* bias, int64_t m,
                                       int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
                                       void* stream) {
-  return gemm_impl("convrot_gemm_int8_tile", false, xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile,
+  return gemm_impl("convrot_gemm_int8_tile", false, DType::kBF16, xq, s_x, wq, s_w, bias, m, n, k, y, acc, tile,
                    stream);
 }
 
@@ -288,8 +328,22 @@ convrot_status convrot_gemm_int8_per_channel_tile(const int8_t* xq, const float*
                                                   const uint16_t* bias, int64_t m, int64_t n,
                                                   int64_t k, uint16_t* y, int32_t* acc, int tile,
                                                   void* stream) {
-  return gemm_impl("convrot_gemm_int8_per_channel_tile", true, xq, s_x, wq, s_w, bias, m, n, k, y,
-                   acc, tile, stream);
+  return gemm_impl("convrot_gemm_int8_per_channel_tile", true, DType::kBF16, xq, s_x, wq, s_w, bias,
+                   m, n, k, y, acc, tile, stream);
+}
+
+convrot_status convrot_gemm_int8_ex(const int8_t* xq, const float* s_x, const int8_t* wq,
+                                    const float* s_w, convrot_scale_mode scale_mode,
+                                    const void* bias, int64_t m, int64_t n, int64_t k, void* y,
+                                    int32_t* acc, convrot_dtype dtype, int tile, void* stream) {
+  const char* fn = "convrot_gemm_int8_ex";
+  bool pc;
+  DType dt;
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  return gemm_impl(fn, pc, dt, xq, s_x, wq, s_w, static_cast<const uint16_t*>(bias), m, n, k,
+                   static_cast<uint16_t*>(y), acc, tile, stream);
 }
 
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k) {
@@ -304,7 +358,8 @@ size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k) {
   return convrot_linear_int8_workspace_for_rows(rows, k);
 }
 
-static convrot_status linear_impl(const char* fn, bool pc, const uint16_t* x, const int8_t* wq,
+static convrot_status linear_impl(const char* fn, bool pc, DType dt, const uint16_t* x,
+                                  const int8_t* wq,
                                   const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
                                   int64_t k, int g, uint64_t rot_seed, uint16_t* y,
                                   void* workspace, size_t workspace_bytes, void* stream) {
@@ -341,9 +396,9 @@ static convrot_status linear_impl(const char* fn, bool pc, const uint16_t* x, co
   hipStream_t st = (hipStream_t)stream;
   for (int64_t r0 = 0; r0 < m; r0 += slice) {
     const int64_t rows = (m - r0) < slice ? (m - r0) : slice;
-    hipError_t e = launch_quantize_rows(x + r0 * k, xq, sx, rows, (int)k, g, sm, st);
+    hipError_t e = launch_quantize_rows(x + r0 * k, xq, sx, rows, (int)k, g, sm, dt, st);
     if (e != hipSuccess) return hip_status(e, fn);
-    e = launch_gemm(xq, sx, wq, s_w, pc, bias, rows, n, k, y + r0 * n, nullptr, st);
+    e = launch_gemm(xq, sx, wq, s_w, pc, bias, rows, n, k, y + r0 * n, nullptr, dt, st);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
@@ -353,7 +408,7 @@ convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const fl
                                    const uint16_t* bias, int64_t m, int64_t n, int64_t k, int g,
                                    uint64_t rot_seed, uint16_t* y, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  return linear_impl("convrot_linear_int8", false, x, wq, s_w, bias, m, n, k, g, rot_seed, y,
+  return linear_impl("convrot_linear_int8", false, DType::kBF16, x, wq, s_w, bias, m, n, k, g, rot_seed, y,
                      workspace, workspace_bytes, stream);
 }
 
@@ -362,8 +417,24 @@ convrot_status convrot_linear_int8_per_channel(const uint16_t* x, const int8_t* 
                                                int64_t n, int64_t k, int g, uint64_t rot_seed,
                                                uint16_t* y, void* workspace,
                                                size_t workspace_bytes, void* stream) {
-  return linear_impl("convrot_linear_int8_per_channel", true, x, wq, s_w, bias, m, n, k, g,
-                     rot_seed, y, workspace, workspace_bytes, stream);
+  return linear_impl("convrot_linear_int8_per_channel", true, DType::kBF16, x, wq, s_w, bias, m, n,
+                     k, g, rot_seed, y, workspace, workspace_bytes, stream);
+}
+
+convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const float* s_w,
+                                      convrot_scale_mode scale_mode, const void* bias, int64_t m,
+                                      int64_t n, int64_t k, int g, uint64_t rot_seed, void* y,
+                                      convrot_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "convrot_linear_int8_ex";
+  bool pc;
+  DType dt;
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  return linear_impl(fn, pc, dt, static_cast<const uint16_t*>(x), wq, s_w,
+                     static_cast<const uint16_t*>(bias), m, n, k, g, rot_seed,
+                     static_cast<uint16_t*>(y), workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

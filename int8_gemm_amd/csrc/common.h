@@ -42,6 +42,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// IEEE half halves of a packed pair -> fp32 (exact).
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+// fp32 -> IEEE half bits, round to nearest even (overflow to inf).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 r = __builtin_convertvector((f2){lo, hi}, h2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// The 16-bit format chosen at compile time: half when F16, else bf16.
+template <bool F16>
+__device__ __forceinline__ float lo16(uint32_t w) { return F16 ? half_lo(w) : bf16lo(w); }
+template <bool F16>
+__device__ __forceinline__ float hi16(uint32_t w) { return F16 ? half_hi(w) : bf16hi(w); }
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+  return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
 __device__ __forceinline__ bool sign_bit(const SignMask& s, int i) {
   return (s.w[i >> 5] >> (i & 31)) & 1u;
 }

@@ -56,7 +56,7 @@ __device__ __forceinline__ v4i frag_from_masks(uint32_t neg, uint32_t nz) {
   return f;
 }
 
-template <int G, bool PC>
+template <int G, bool PC, bool F16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1))) void dequant_kernel(const int8_t* __restrict__ wq,
                                                       const float* __restrict__ s_w,
                                                       int64_t nrows, int vrows_per_ch,
@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1)
       // them as bf16 in this wave's LDS rows
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const u2 v = {pack_bf16x2((float)acc[4 * a + 0] * c, (float)acc[4 * a + 1] * c),
-                      pack_bf16x2((float)acc[4 * a + 2] * c, (float)acc[4 * a + 3] * c)};
+        const u2 v = {pack16x2<F16>((float)acc[4 * a + 0] * c, (float)acc[4 * a + 1] * c),
+                      pack16x2<F16>((float)acc[4 * a + 2] * c, (float)acc[4 * a + 3] * c)};
         *reinterpret_cast<u2*>(so + jl * OSTR + 2 * (32 * jw + 8 * a + 4 * kh)) = v;
       }
     }
@@ -211,15 +211,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1)
 }  // namespace
 
 template <int G>
-static void launch_g(bool pc, int64_t blocks, const int8_t* wq, const float* s_w, int64_t nrows,
-                     int vrows_per_ch, const SignMask& sm, uint16_t* w_out, hipStream_t st) {
-  auto kern = pc ? dequant_kernel<G, true> : dequant_kernel<G, false>;
+static void launch_g(bool pc, bool f16, int64_t blocks, const int8_t* wq, const float* s_w,
+                     int64_t nrows, int vrows_per_ch, const SignMask& sm, uint16_t* w_out,
+                     hipStream_t st) {
+  auto kern = f16 ? (pc ? dequant_kernel<G, true, true> : dequant_kernel<G, false, true>)
+                  : (pc ? dequant_kernel<G, true, false> : dequant_kernel<G, false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w, nrows,
                      vrows_per_ch, 1.0 / (double)vrows_per_ch, sm, w_out);
 }
 
 hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,
-                          int64_t k, int g, const SignMask& sm, uint16_t* w_out, hipStream_t st) {
+                          int64_t k, int g, const SignMask& sm, uint16_t* w_out, DType dt,
+                          hipStream_t st) {
   const int64_t ne = n * k;
   if (ne == 0) return hipSuccess;
   const int R = g > 32 ? g : 32;
@@ -233,11 +236,12 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channe
   const int64_t cap = (int64_t)kNumCUs * CONVROT_DEQUANT_BLOCKS_PER_CU;  // persistent blocks
   const int64_t blocks = chunks < cap ? chunks : cap;
   const int vrows_per_ch = (int)(k / R);  // K % R == 0 for every supported (K, g)
+  const bool pc = sw_per_channel, f16 = dt == DType::kF16;
   switch (g) {
-    case 4: launch_g<4>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 16: launch_g<16>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 64: launch_g<64>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    default: launch_g<256>(sw_per_channel, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 4: launch_g<4>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 16: launch_g<16>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 64: launch_g<64>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    default: launch_g<256>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
   }
   return hipGetLastError();
 }

@@ -80,8 +80,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // PC: s_w holds one scale per output column n (per output channel of the
-// weight) instead of one for the tensor.
-template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP, bool PC>
+// weight) instead of one for the tensor. F16: bias and y are IEEE half
+// instead of bf16.
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP, bool PC, bool F16>
 __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_x, const int8_t* __restrict__ wq,
     const float* __restrict__ s_w, const uint16_t* __restrict__ bias, int M, int N, int K,
@@ -386,13 +387,13 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
         }
         if (bias) {
           const u2 bb = *reinterpret_cast<const u2*>(bias + n);
-          f[0] = f[0] + bf16lo(bb.x);
-          f[1] = f[1] + bf16hi(bb.x);
-          f[2] = f[2] + bf16lo(bb.y);
-          f[3] = f[3] + bf16hi(bb.y);
+          f[0] = f[0] + lo16<F16>(bb.x);
+          f[1] = f[1] + hi16<F16>(bb.x);
+          f[2] = f[2] + lo16<F16>(bb.y);
+          f[3] = f[3] + hi16<F16>(bb.y);
         }
         if (y) {
-          const u2 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+          const u2 o = {pack16x2<F16>(f[0], f[1]), pack16x2<F16>(f[2], f[3])};
           *reinterpret_cast<u2*>(y + (int64_t)m * N + n) = o;
         }
       }
@@ -404,13 +405,13 @@ struct TileCfg {
   int bm, bn, ns, per_cu;
 };
 
-template <bool PC, int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
+template <bool PC, bool F16, int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
 hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                       const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
                       hipStream_t st) {
   constexpr int lds_bytes = NS * (BM + BN) * BK;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
-  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP, PC>;
+  auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP, PC, F16>;
   static bool attr = false;  // benign race: the call is idempotent
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -454,43 +455,47 @@ TileCfg choose_tile(int64_t m, int64_t n) {
 // 128-byte K-steps (whole L2 lines per request): a two-stage ring for the
 // 256 and 128 tiles (64 and 32 KB stages), three stages and four producer
 // waves for the 192 tile. Otherwise 64-byte K-steps with deeper rings.
-template <bool PC>
+template <bool PC, bool F16>
 static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
                               const float* s_w, const uint16_t* bias, int M, int N, int K,
                               uint16_t* y, int32_t* acc, hipStream_t st) {
   switch (tile) {
     case 256:
       if (K % 128 == 0)
-        return launch_cfg<PC, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<PC, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, F16, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, F16, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     case 192:
       if (K % 128 == 0)
-        return launch_cfg<PC, 192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
+        return launch_cfg<PC, F16, 192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
                                                           st);
-      return launch_cfg<PC, 192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, F16, 192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
     default:
       if (K % 128 == 0)
-        return launch_cfg<PC, 128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<PC, 128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, F16, 128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+      return launch_cfg<PC, F16, 128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
   }
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                        bool sw_per_channel, const uint16_t* bias, int64_t m, int64_t n, int64_t k,
-                       uint16_t* y, int32_t* acc, hipStream_t st) {
-  return launch_gemm_tile(xq, s_x, wq, s_w, sw_per_channel, bias, m, n, k, y, acc, 0, st);
+                       uint16_t* y, int32_t* acc, DType dt, hipStream_t st) {
+  return launch_gemm_tile(xq, s_x, wq, s_w, sw_per_channel, bias, m, n, k, y, acc, 0, dt, st);
 }
 
 hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
                             const float* s_w, bool sw_per_channel, const uint16_t* bias,
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
-                            hipStream_t st) {
+                            DType dt, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
   if (tile == 0) tile = choose_tile(m, n).bm;
+  const int M = (int)m, N = (int)n, K = (int)k;
+  if (dt == DType::kF16)
+    return sw_per_channel
+               ? launch_tile<true, true>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st)
+               : launch_tile<false, true>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
   return sw_per_channel
-             ? launch_tile<true>(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc, st)
-             : launch_tile<false>(tile, xq, s_x, wq, s_w, bias, (int)m, (int)n, (int)k, y, acc,
-                                  st);
+             ? launch_tile<true, false>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st)
+             : launch_tile<false, false>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
 }
 
 }  // namespace convrot

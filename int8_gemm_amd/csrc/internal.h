@@ -5,10 +5,13 @@
 
 namespace convrot {
 
+// 16-bit float format of activations, bias and outputs.
+enum class DType { kBF16 = 0, kF16 = 1 };
+
 // Rotate + quantize rows (per-row scales): fast kernel, then the exact kernel
-// over the rows it deferred.
+// over the rows it deferred (bf16 only: half rows are never deferred).
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
-                                int g, const SignMask& sm, hipStream_t st);
+                                int g, const SignMask& sm, DType dt, hipStream_t st);
 // Same result through the exact kernel only (used by tests of the fast path).
 hipError_t launch_quantize_rows_exact(const uint16_t* x, int8_t* xq, float* s, int64_t rows,
                                       int K, int g, const SignMask& sm, hipStream_t st);
@@ -16,19 +19,21 @@ hipError_t launch_quantize_rows_exact(const uint16_t* x, int8_t* xq, float* s, i
 // absmax accumulator until the last launch).
 hipError_t launch_quantize_tensor(const uint16_t* w, int8_t* wq, float* s_w, int64_t rows, int K,
                                   int g, const SignMask& sm, hipStream_t st);
-// W_hat = bf16(float(S) * RN(s_w * 2^-log2(sqrt g))), S = (Wq . D) . H per group;
-// with sw_per_channel, row r of the weight uses s_w[r].
+// W_hat = RN16(float(S) * RN(s_w * 2^-log2(sqrt g))), S = (Wq . D) . H per
+// group, RN16 to bf16 or half (dt); with sw_per_channel, row r uses s_w[r].
 hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,
-                          int64_t k, int g, const SignMask& sm, uint16_t* w_out, hipStream_t st);
-// acc = xq . wq^T (int32); y = bf16(RN(RN(float(acc) * s_w) * s_x[m]) [+ bias[n]]);
-// with sw_per_channel, column n uses s_w[n] (s_w then 16-byte aligned).
+                          int64_t k, int g, const SignMask& sm, uint16_t* w_out, DType dt,
+                          hipStream_t st);
+// acc = xq . wq^T (int32); y = RN16(RN(RN(float(acc) * s_w) * s_x[m]) [+ bias[n]]),
+// bias and y in dt; with sw_per_channel, column n uses s_w[n] (s_w then
+// 16-byte aligned).
 hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                        bool sw_per_channel, const uint16_t* bias, int64_t m, int64_t n, int64_t k,
-                       uint16_t* y, int32_t* acc, hipStream_t st);
+                       uint16_t* y, int32_t* acc, DType dt, hipStream_t st);
 // The same GEMM with a forced block tile (128, 192 or 256; 0 = automatic).
 hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
                             const float* s_w, bool sw_per_channel, const uint16_t* bias,
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
-                            hipStream_t st);
+                            DType dt, hipStream_t st);
 
 }  // namespace convrot

@@ -28,6 +28,11 @@
 //     has at least 27 bits; otherwise the element is at least 2^16 times
 //     below the row's absmax and quantizes to 0 whatever its fp32 value.
 //
+// IEEE half inputs (the fast kernel's F16 form): every half value is a
+// multiple of 2^-24 below 2^16, so a group's signed sums are multiples of
+// 2^-24 below 2^24 and every float64 partial sum is exact. No half row is
+// ever deferred (its absmax also lies far inside the scaling range).
+//
 // Quantization (per row or per tensor): s = RN(amax/127), inv = RN(127/amax)
 // (both operands scaled by 2^64 first when amax < 2^-64),
 // q = rint_even(RN(x_r * inv)); |q| <= 127 always; amax == 0 gives s = q = 0.
@@ -149,13 +154,13 @@ __device__ __forceinline__ int group_span(uint32_t mxbits, uint32_t mnbits) {
 // of T = K/64 lanes; a block holds rows_per_block rows (one "batch") at a
 // time and walks batches blockIdx.x, blockIdx.x + gridDim.x, ... (persistent
 // grid). The next batch's bf16 words are loaded into registers while the
-// current batch is transformed. The per-row max and flag go through LDS
+// current batch is transformed (16-bit words: bf16, or half when F16). The per-row max and flag go through LDS
 // slots used round-robin over 3 batches, so one barrier per batch suffices:
 // the slot reset after batch b's barrier is that of batch b-1 (whose readers
 // all passed the barrier) and it is next written after batch b+1's barrier.
 // ============================================================================
 
-template <int G>
+template <int G, bool F16>
 __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     const uint16_t* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ scale,
     int64_t rows, int K, int T, int rows_per_block, int64_t nbatches, SignMask sm) {
@@ -225,9 +230,9 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     uint32_t wn[32];
     load(batch + gridDim.x, wn);
 
-    // ---- exponent span per group ----
+    // ---- exponent span per group (half groups are always exact) ----
     bool flagged = false;
-    {
+    if constexpr (!F16) {
       constexpr int DW = (G >= CH ? CH : G) / 2;  // dwords per (lane part of a) group
 #pragma unroll
       for (int gidx = 0; gidx < NGL; ++gidx) {
@@ -249,8 +254,8 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     double v[CH];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      v[2 * i] = (double)bf16lo(w[i]);
-      v[2 * i + 1] = (double)bf16hi(w[i]);
+      v[2 * i] = (double)(F16 ? half_lo(w[i]) : bf16lo(w[i]));
+      v[2 * i + 1] = (double)(F16 ? half_hi(w[i]) : bf16hi(w[i]));
     }
     fwht_inlane<G, CH>(v);
     if constexpr (G == 256) {
@@ -713,13 +718,14 @@ constexpr int kFastWavesPerCU = CONVROT_FAST_WAVES_PER_CU;
 
 template <int G>
 hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
-                       const SignMask& sm, hipStream_t st) {
+                       const SignMask& sm, bool f16, hipStream_t st) {
   const TeamShape ts = team_shape(K / 64);
   const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
   const int64_t cap = (int64_t)kNumCUs * kFastWavesPerCU / (ts.block / 64);
   const int64_t blocks = nbatches < cap ? nbatches : cap;
-  hipLaunchKernelGGL(rotate_quant_fast_kernel<G>, dim3((unsigned)blocks), dim3(ts.block), 0, st,
-                     x, xq, s, rows, K, ts.T, ts.rpb, nbatches, sm);
+  auto kern = f16 ? rotate_quant_fast_kernel<G, true> : rotate_quant_fast_kernel<G, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ts.block), 0, st, x, xq, s, rows, K,
+                     ts.T, ts.rpb, nbatches, sm);
   return hipGetLastError();
 }
 
@@ -751,16 +757,17 @@ hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tenso
 }  // namespace
 
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
-                                int g, const SignMask& sm, hipStream_t st) {
+                                int g, const SignMask& sm, DType dt, hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  const bool f16 = dt == DType::kF16;
   hipError_t e;
   switch (g) {
-    case 4: e = launch_fast<4>(x, xq, s, rows, K, sm, st); break;
-    case 16: e = launch_fast<16>(x, xq, s, rows, K, sm, st); break;
-    case 64: e = launch_fast<64>(x, xq, s, rows, K, sm, st); break;
-    default: e = launch_fast<256>(x, xq, s, rows, K, sm, st); break;
+    case 4: e = launch_fast<4>(x, xq, s, rows, K, sm, f16, st); break;
+    case 16: e = launch_fast<16>(x, xq, s, rows, K, sm, f16, st); break;
+    case 64: e = launch_fast<64>(x, xq, s, rows, K, sm, f16, st); break;
+    default: e = launch_fast<256>(x, xq, s, rows, K, sm, f16, st); break;
   }
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || f16) return e;  // half rows are never deferred
   switch (g) {
     case 4: return launch_exact<4>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);
     case 16: return launch_exact<16>(x, xq, s, nullptr, rows, K, sm, kRowDeferred, st);

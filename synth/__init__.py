@@ -46,14 +46,21 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half (nearest, ties to even); return uint16
+    bits. Input preparation only; inputs here stay below half's maximum."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _n_out(frac: float, k: int) -> int:
     return int(round(frac * k))
 
 
 def activations(m: int, k: int, seed: int, *, outlier_frac: float = 0.0,
                 outlier_mult: float = 1.0, n_outliers: int | None = None,
-                gelu: bool = False) -> np.ndarray:
-    """Token activations x [m, k] as bf16 bits.
+                gelu: bool = False, fmt: str = "bf16") -> np.ndarray:
+    """Token activations x [m, k] as bf16 bits (fmt="f16": IEEE half bits of
+    the same float32 draws).
 
     N(0,1) values; a seeded set of input channels (columns) multiplied by
     `outlier_mult`. With `gelu=True` the tanh-approximation GELU is applied
@@ -70,7 +77,7 @@ def activations(m: int, k: int, seed: int, *, outlier_frac: float = 0.0,
         zz = z.astype(np.float64)
         zz = 0.5 * zz * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (zz + 0.044715 * zz ** 3)))
         z = zz.astype(np.float32)
-    return f32_to_bf16_bits(z)
+    return f32_to_f16_bits(z) if fmt == "f16" else f32_to_bf16_bits(z)
 
 
 def weights(n: int, k: int, seed: int, *, std: float = 0.02, outlier_frac: float = 0.0,
@@ -112,12 +119,13 @@ class Layer:
     x_n_outliers: int | None = None
     w_n_outliers: int | None = None
 
-    def x(self, rows: int | None = None) -> np.ndarray:
-        """Activations. With `rows`, the full matrix is drawn (so the values
-        are those of the full workload) and its first rows are returned."""
+    def x(self, rows: int | None = None, fmt: str = "bf16") -> np.ndarray:
+        """Activations (bf16 bits, or half bits with fmt="f16"). With `rows`,
+        the full matrix is drawn (so the values are those of the full
+        workload) and its first rows are returned."""
         a = activations(self.m, self.k, self.x_seed, outlier_frac=self.x_outlier_frac,
                         outlier_mult=self.x_outlier_mult, n_outliers=self.x_n_outliers,
-                        gelu=self.x_gelu)
+                        gelu=self.x_gelu, fmt=fmt)
         return a if rows is None else a[:rows]
 
     def w(self) -> np.ndarray:

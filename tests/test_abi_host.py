@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 2
+    assert cr.convrot_abi_version() == 3
     for s in range(7):
         assert cr.convrot_status_string(s)
 
@@ -180,3 +180,31 @@ def test_per_channel_scale_vector_checks(lib):
     assert _status(lib, "convrot_gemm_int8_per_channel", FAKE, ctypes.c_void_p(1 << 22),
                    ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), None, 0, n, k,
                    ctypes.c_void_p(1 << 28), None, None) == 0
+
+
+def test_ex_entry_points_reject_unknown_enums(lib):
+    """dtype and scale_mode values outside their enums fail before any HIP call"""
+    n, k = 64, 256
+    assert _status(lib, "convrot_quantize_activations_ex", FAKE, 2, 8, k, 256, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28), None) == 1
+    assert _status(lib, "convrot_dequant_derotate_ex", FAKE, ctypes.c_void_p(1 << 24), 2, n, k,
+                   256, 1, ctypes.c_void_p(1 << 28), 0, None) == 1
+    assert _status(lib, "convrot_dequant_derotate_ex", FAKE, ctypes.c_void_p(1 << 24), 0, n, k,
+                   256, 1, ctypes.c_void_p(1 << 28), -1, None) == 1
+    assert _status(lib, "convrot_gemm_int8_ex", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), 0, None, 8, n, k,
+                   ctypes.c_void_p(1 << 28), None, 7, 0, None) == 1
+    assert _status(lib, "convrot_linear_int8_ex", FAKE, ctypes.c_void_p(1 << 24),
+                   ctypes.c_void_p(1 << 26), 5, None, 8, n, k, 256, 1, ctypes.c_void_p(1 << 28),
+                   1, ctypes.c_void_p(1 << 32), 1 << 20, None) == 1
+    # valid enums reach the ordinary checks (here: a bad group, and a
+    # per-channel scale that is only 4-byte aligned)
+    assert _status(lib, "convrot_quantize_activations_ex", FAKE, 1, 8, k, 512, 1,
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28), None) == 2
+    assert _status(lib, "convrot_gemm_int8_ex", FAKE, ctypes.c_void_p(1 << 22),
+                   ctypes.c_void_p(1 << 24), ctypes.c_void_p((1 << 26) + 4), 1, None, 8, n, k,
+                   ctypes.c_void_p(1 << 28), None, 1, 0, None) == 4
+    # m == 0 with half: a no-op
+    assert _status(lib, "convrot_linear_int8_ex", FAKE, ctypes.c_void_p(1 << 24),
+                   ctypes.c_void_p(1 << 26), 0, None, 0, n, k, 256, 1, ctypes.c_void_p(1 << 28),
+                   1, ctypes.c_void_p(1 << 32), 1 << 20, None) == 0

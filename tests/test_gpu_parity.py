@@ -393,3 +393,109 @@ def test_per_channel_binding_rejects_wrong_scale_length():
         buf = torch.ones(40, device=DEV)
         cr.convrot_dequant_derotate_per_channel(wq, buf[1:33], 256)
     assert e.value.status_name == "CONVROT_E_MISALIGNED"
+
+
+# --------------------------------------------------------------------------
+# FP16 activations, bias, outputs and W_hat (the *_ex entry points)
+# --------------------------------------------------------------------------
+
+def dev_f16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(DEV)
+
+
+@pytest.mark.parametrize("layer,g", REDUCED, ids=IDS)
+def test_f16_quantize_activations_bitexact(layer, g):
+    _announce(f"f16 quantize_activations {layer.name} g={g}")
+    hb = layer.x(fmt="f16")
+    xq, sx = cr.convrot_quantize_activations_ex(dev_f16(hb), g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(hb, g, SEED, "f16")
+    assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("g", GS)
+def test_f16_edge_rows(g):
+    """the widest spans half allows, zeros, subnormals, max values, ties"""
+    _announce(f"f16 edge rows g={g}")
+    rng = np.random.default_rng(50 + g)
+    k = 512
+    rows = [np.zeros(k), np.full(k, -0.0), np.full(k, 65504.0), np.full(k, 2.0 ** -24)]
+    r = rng.standard_normal(k) * 2.0 ** rng.integers(-26, 16, k)
+    rows.append(np.clip(r, -65504, 65504))
+    r = np.zeros(k); r[::64] = 1.0; r[1::64] = 2.0 ** -11; r[2::64] = 2.0 ** -24
+    rows.append(r)
+    r = rng.standard_normal(k); r[::9] = 2.0 ** -24; r[4::31] = -65504.0
+    rows.append(r)
+    hb = np.array(rows).astype(np.float16).view(np.uint16)
+    xq, sx = cr.convrot_quantize_activations_ex(dev_f16(hb), g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(hb, g, SEED, "f16")
+    assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("tile", [0, 128, 192, 256])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (257, 272, 320), (300, 400, 1152)])
+def test_f16_gemm_shapes(m, n, k, tile, per_channel):
+    _announce(f"f16 gemm {m}x{n}x{k} tile={tile} pc={per_channel}")
+    rng = np.random.default_rng(m + 3 * n)
+    xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    wq = rng.integers(-127, 128, (n, k)).astype(np.int8)
+    sx = (rng.random(m) * 1e-2).astype(np.float32)
+    sx[0] = np.float32(50.0)          # row 0 overflows half in places: inf
+    sw = (rng.random(n) * 1e-2).astype(np.float32) if per_channel else np.float32(4e-3)
+    bias = synth.f32_to_f16_bits(rng.standard_normal(n).astype(np.float32))
+    for b in (None, bias):
+        y, acc = cr.convrot_gemm_int8_ex(
+            torch.from_numpy(xq).to(DEV), torch.from_numpy(sx).to(DEV),
+            torch.from_numpy(wq).to(DEV),
+            torch.from_numpy(np.atleast_1d(sw).astype(np.float32)).to(DEV),
+            None if b is None else dev_f16(b), per_channel=per_channel, dtype=torch.float16,
+            want_acc=True, tile=tile)
+        acc_ref = oracle.gemm_int32(xq, wq)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert np.array_equal(host_bits(y), oracle.epilogue(acc_ref, sw, sx, b, "f16"))
+
+
+@pytest.mark.parametrize("layer,g", REDUCED[:4] + REDUCED[-2:], ids=IDS[:4] + IDS[-2:])
+def test_f16_linear_and_dequant(layer, g):
+    _announce(f"f16 linear + dequant {layer.name} g={g}")
+    hb = layer.x(fmt="f16")
+    for per_channel in (False, True):
+        wb = layer.w()
+        wq_ref, s_ref = (oracle.quantize_weights_per_channel if per_channel
+                         else oracle.quantize_weights)(wb, g, SEED)
+        bias = synth.f32_to_f16_bits(
+            np.random.default_rng(9).standard_normal(layer.n).astype(np.float32))
+        y_ref, _, sx_ref, acc_ref = oracle.linear_int8(hb, wq_ref, s_ref, g, SEED, bias, "f16")
+        wq = torch.from_numpy(wq_ref).to(DEV)
+        s_w = torch.from_numpy(np.atleast_1d(s_ref).astype(np.float32)).to(DEV)
+        x = dev_f16(hb)
+        got = host_bits(cr.convrot_linear_int8_ex(x, wq, s_w, g, SEED, dev_f16(bias),
+                                                  per_channel=per_channel))
+        assert np.array_equal(got, y_ref), per_channel
+        ref = oracle.linear_int8_reference_f64(acc_ref, s_ref, sx_ref, bias, "f16")
+        assert oracle.rel_frobenius(oracle.f16_to_f64(got), ref) < 1e-2
+        w_hat = cr.convrot_dequant_derotate_ex(wq, s_w, g, SEED, per_channel=per_channel,
+                                               out_dtype=torch.float16)
+        assert np.array_equal(host_bits(w_hat),
+                              oracle.dequant_derotate(wq_ref, s_ref, g, SEED, "f16"))
+        # the default path in half, consumed by a float32 matmul
+        y_deq = (x.float() @ w_hat.float().t()).to(torch.float16)
+        ref_deq = oracle.dequant_linear_reference_f64(hb, wq_ref, s_ref, g, SEED, dtype="f16")
+        assert oracle.rel_frobenius(oracle.f16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
+
+
+def test_ex_bf16_matches_named_entry_points():
+    """the general forms with bf16 reproduce the named calls bit for bit"""
+    _announce("ex bf16 vs named")
+    layer, g = synth.ZIMAGE_ATTN.scaled(m=300, n=272), 256
+    x = dev_bf16(layer.x())
+    wq, s_w = cr.convrot_quantize_weights(dev_bf16(layer.w()), g, SEED)
+    assert torch.equal(cr.convrot_linear_int8_ex(x, wq, s_w, g, SEED),
+                       cr.convrot_linear_int8(x, wq, s_w, g, SEED))
+    xq1, sx1 = cr.convrot_quantize_activations_ex(x, g, SEED)
+    xq2, sx2 = cr.convrot_quantize_activations(x, g, SEED)
+    assert torch.equal(xq1, xq2) and torch.equal(sx1, sx2)
+    assert torch.equal(cr.convrot_dequant_derotate_ex(wq, s_w, g, SEED),
+                       cr.convrot_dequant_derotate(wq, s_w, g, SEED))

@@ -31,3 +31,15 @@ def test_student_t_columns_heavy_tailed():
 def test_bf16_round_trip():
     v = np.array([1.0, 1.0078125, -2.5, 0.0, 2.0 ** 127], dtype=np.float32)
     assert np.array_equal(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)), v)
+
+
+def test_f16_activations_are_the_same_draws():
+    layer = synth.TINY
+    hb = layer.x(fmt="f16")
+    bb = layer.x()
+    a = hb.view(np.float16).astype(np.float32)
+    b = synth.bf16_bits_to_f32(bb)
+    assert hb.dtype == np.uint16 and hb.shape == bb.shape
+    assert np.isfinite(a).all()
+    # both round the same float32 draws: half keeps 3 more bits
+    assert np.abs(a - b).max() <= 2.0 ** -8 * np.abs(b).max()

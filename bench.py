@@ -38,6 +38,7 @@ PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20
 SLEEP_CYCLES = 50_000_000  # GPU-side hold before a timed batch of launches
+WARM_LAUNCHES = 5  # untimed launches between the sleep and the first event
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_zimage_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "int8_gemm_amd", "csrc", "gemm.hip")
 
@@ -76,22 +77,28 @@ def _traffic(n_launch_units: float):
 def _events_time(fn, reps, stream):
     """GPU duration per launch from HIP events recorded on `stream`. The stream
     is first held by a GPU sleep long enough for the host to enqueue every
-    call, so the events bracket the kernels alone, not host launch gaps.
-    Returns (mean, min, median) in ms: the mean over one batch of `reps`
-    back-to-back launches between two events (per-event overhead amortised,
-    as a kernel trace sees it), min and median over launches bracketed one by
-    one."""
+    call, so the events bracket the kernels alone, not host launch gaps; a
+    few untimed launches after the sleep bring the clocks back up before the
+    first event. Returns (mean, min, median) in ms: the mean over a batch of
+    `reps` back-to-back launches between two events (per-event overhead
+    amortised, as a kernel trace sees it; the median of 3 such batches), min
+    and median over launches bracketed one by one."""
     import torch
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(SLEEP_CYCLES)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(reps):
-        fn(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    mean = t0.elapsed_time(t1) / reps
+    means = []
+    for _ in range(3):
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(SLEEP_CYCLES)
+        for i in range(WARM_LAUNCHES):
+            fn(i)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(reps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        means.append(t0.elapsed_time(t1) / reps)
+    mean = sorted(means)[1]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     with torch.cuda.stream(stream):
@@ -200,7 +207,7 @@ def main():
     gemm_ms, gemm_min, gemm_med = _events_time(
         lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=y), reps, stream)
     tiles = {}
-    for t in (128, 192, 256):
+    for t in (128, 192, 256, 384):
         t_ms, _, _ = _events_time(
             lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=y, tile=t), reps, stream)
         tiles[str(t)] = round(2.0 * m * n * k / (t_ms * 1e-3) / 1e12, 1)
@@ -227,6 +234,19 @@ def main():
                                                           out=outs[i % nrot_w]), reps, stream)
     torch.cuda.synchronize()
     del wqs, outs, wqs_pc, wq_pc
+
+    # ---- FP16 activations and outputs: the same layer with x, y in half ----
+    xh0 = torch.from_numpy(layer.x(fmt="f16").view(np.int16)).view(torch.float16).to(dev)
+    xhs = [xh0] + [xh0.clone() for _ in range(nrot_x - 1)]
+    yh = torch.empty((m, n), dtype=torch.float16, device=dev)
+    h_lin_ms, _, _ = _events_time(
+        lambda i: cr.convrot_linear_int8_ex(xhs[i % nrot_x], wq, s_w, g, seed, workspace=ws,
+                                            out=yh), reps, stream)
+    h_act_ms, _, _ = _events_time(
+        lambda i: cr.convrot_quantize_activations_ex(xhs[i % nrot_x], g, seed, xq=xq, s_x=sx),
+        reps, stream)
+    torch.cuda.synchronize()
+    del xhs, xh0, yh
 
     # ---- dequant over the 60-layer stack: 60 + 60 distinct int8 buffers of
     # the two stack shapes, one dequant each per pass, outputs rotated over 4 ----
@@ -309,6 +329,11 @@ def main():
                                       / PEAK_HBM_GBS, 4),
             "linear_avg_ms": round(pc_lin_ms, 5), "gemm_avg_ms": round(pc_gemm_ms, 5),
             "dequant_avg_ms": round(pc_deq_ms, 5)},
+        "f16": {
+            "linear_TOPS": round(ops / (h_lin_ms * 1e-3) / 1e12, 1),
+            "act_quant_GB/s": round(act_bytes / (h_act_ms * 1e-3) / 1e9, 1),
+            "act_quant_frac_hbm": round(act_bytes / (h_act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "linear_avg_ms": round(h_lin_ms, 5), "act_quant_avg_ms": round(h_act_ms, 5)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

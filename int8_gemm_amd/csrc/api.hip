@@ -278,8 +278,10 @@ static convrot_status gemm_impl(const char* fn, bool pc, DType dt, const int8_t*
                                 const int8_t* wq, const float* s_w, const uint16_t* bias,
                                 int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc,
                                 int tile, void* stream) {
-  if (tile != 0 && tile != 128 && tile != 192 && tile != 256)
+  if (tile != 0 && tile != 128 && tile != 192 && tile != 256 && tile != 384)
     return fail(CONVROT_E_INVALID_ARG, "%s: tile=%d not supported", fn, tile);
+  if (tile == 384 && k % 128 != 0)
+    return fail(CONVROT_E_INVALID_ARG, "%s: the 384 x 192 tile needs k %% 128 == 0", fn);
   if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (convrot_status s = check_gemm(fn, m, n, k)) return s;
   if (m == 0) return ok();  // the M-sized buffers may be null

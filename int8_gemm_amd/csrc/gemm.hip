@@ -2,12 +2,15 @@
 //
 // acc[m, n] = sum_k xq[m, k] * wq[n, k] (exact int32: |acc| <= 127^2 K < 2^31)
 // y[m, n]   = bf16(RN32(RN32(float(acc) * s_w) * s_x[m]) [+ bias[n] in fp32])
+//             (s_w per tensor, or s_w[n] per output channel; bias and y in
+//             bf16 or IEEE half)
 //
 // This is the int8 tensor-core multiply of int8_compute (Invoke docs
 // "int8 Compute", introduction: the input is quantized per token and int8 is
 // multiplied by int8); the pages run it through Triton on NVIDIA, this is a
 // gfx950 design of its own:
-//   * block tile BM x BN: 256x256 with 8 compute waves in a 2 x 4 grid,
+//   * block tile BM x BN: 384x192 (K % 128 == 0) with 8 compute waves in a
+//     4 x 2 grid, 256x256 with 8 compute waves in a 2 x 4 grid,
 //     192x192 with 4 compute waves (2 x 2) plus 4 producer waves, 128x128
 //     with 4 waves (2 x 2, two blocks per CU); v_mfma_i32_32x32x32_i8 (on
 //     gfx950 it sustains the full int8 rate, the 16x16x64 form about half)
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // rows RPI*q .. RPI*q+RPI-1 (weights first, then activations); lane ->
   // row RPI*q + lane/CPR, 16-byte chunk lane%CPR (whole L2 lines for BK=128) ----
   // 32-bit byte offsets from the tile's first weight / activation row
-  // (below BM*K <= 256 * 133144 < 2^31); the 64-bit tile base pointer and the
+  // (below BM*K <= 384 * 133144 < 2^31); the 64-bit tile base pointer and the
   // K-step offset go in SGPRs. Rows past the matrix edge re-read its last row.
   const int8_t* wtile = wq + (int64_t)n0 * K;
   const int8_t* xtile = xq + (int64_t)m0 * K;
@@ -427,20 +430,23 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 }
 
 // Pick the tile whose estimated time is least: rounds of concurrent tiles
-// over 256 CUs times the work of one tile, with a small penalty for the
-// lower operand reuse of smaller tiles.
-TileCfg choose_tile(int64_t m, int64_t n) {
-  const TileCfg cands[] = {{256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
-  // relative throughput per tile round (measured on full rounds)
-  const double eff[] = {1.0, 0.9, 0.8};
-  TileCfg best = cands[0];
+// over 256 CUs times the measured duration of one round of that tile
+// (relative; the operand stream per CU bounds every tile, so a round's
+// duration follows the tile's operand bytes and its L2 behaviour). The
+// 384 x 192 tile exists for K % 128 == 0 only.
+TileCfg choose_tile(int64_t m, int64_t n, int64_t k) {
+  const TileCfg cands[] = {{384, 192, 2, 1}, {256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
+  // duration of one full round relative to the 192 tile's (4608-row layers)
+  const double round_t[] = {1.75, 1.336, 1.0, 1.0};
+  TileCfg best = cands[2];
   double best_t = 1e300;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < 4; ++c) {
     const TileCfg& t = cands[c];
+    if (t.bm == 384 && k % 128 != 0) continue;
     const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
     const int64_t slots = 256LL * t.per_cu;
     const int64_t rounds = (tiles + slots - 1) / slots;
-    const double time = (double)rounds * t.bm * t.bn * t.per_cu / eff[c];
+    const double time = (double)rounds * round_t[c];
     if (time < best_t * 0.999) {
       best_t = time;
       best = t;
@@ -453,8 +459,9 @@ TileCfg choose_tile(int64_t m, int64_t n) {
 
 // One configuration per tile size. When K allows, every tile streams
 // 128-byte K-steps (whole L2 lines per request): a two-stage ring for the
-// 256 and 128 tiles (64 and 32 KB stages), three stages and four producer
-// waves for the 192 tile. Otherwise 64-byte K-steps with deeper rings.
+// 384 x 192, 256 and 128 tiles (72, 64 and 32 KB stages), three stages and
+// four producer waves for the 192 tile. Otherwise 64-byte K-steps with
+// deeper rings (the 384 x 192 tile then does not exist).
 template <bool PC, bool F16>
 static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
                               const float* s_w, const uint16_t* bias, int M, int N, int K,
@@ -464,6 +471,9 @@ static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, cons
       if (K % 128 == 0)
         return launch_cfg<PC, F16, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
       return launch_cfg<PC, F16, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+    case 384:  // 384 x 192 (K % 128 == 0 only)
+      return launch_cfg<PC, F16, 384, 192, 128, 4, 2, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
+                                                            st);
     case 192:
       if (K % 128 == 0)
         return launch_cfg<PC, F16, 192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
@@ -487,7 +497,7 @@ hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
                             DType dt, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (tile == 0) tile = choose_tile(m, n).bm;
+  if (tile == 0) tile = choose_tile(m, n, k).bm;
   const int M = (int)m, N = (int)n, K = (int)k;
   if (dt == DType::kF16)
     return sw_per_channel

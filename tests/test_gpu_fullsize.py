@@ -52,10 +52,10 @@ def f32_bits(a) -> np.ndarray:
 
 
 def sample_rows(count: int, extra=(), n_random: int = 8, seed: int = 11) -> np.ndarray:
-    """First/last rows, rows at 128/192/256-row tile edges (including the
+    """First/last rows, rows at 128/192/256/384-row tile edges (including the
     last, ragged tile), the given extra rows and a few random ones."""
-    rows = {0, 1, 127, 128, 191, 192, 255, 256, count - 2, count - 1}
-    for t in (128, 192, 256):
+    rows = {0, 1, 127, 128, 191, 192, 255, 256, 383, 384, count - 2, count - 1}
+    for t in (128, 192, 256, 384):
         last = (count - 1) // t * t
         rows.update({last - 1, last})
     rows.update(extra)

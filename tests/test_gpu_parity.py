@@ -214,12 +214,20 @@ def test_edge_weights(g):
         assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
 
 
-@pytest.mark.parametrize("tile", [0, 128, 192, 256])
+@pytest.mark.parametrize("tile", [0, 128, 192, 256, 384])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (2, 32, 128), (255, 16, 192), (257, 272, 320),
                                    (33, 1040, 64), (512, 512, 4096), (400, 592, 384),
-                                   (300, 400, 1152), (300, 400, 1088)])
+                                   (300, 400, 1152), (300, 400, 1088), (800, 208, 256)])
 def test_gemm_shapes(m, n, k, tile):
     _announce(f"gemm shape {m}x{n}x{k} tile={tile}")
+    if tile == 384 and k % 128:
+        with pytest.raises(cr.ConvrotError) as e:   # the 384 x 192 tile needs K % 128 == 0
+            cr.convrot_gemm_int8(torch.zeros((m, k), dtype=torch.int8, device=DEV),
+                                 torch.ones(m, device=DEV),
+                                 torch.zeros((n, k), dtype=torch.int8, device=DEV),
+                                 torch.ones(1, device=DEV), tile=tile)
+        assert e.value.status_name == "CONVROT_E_INVALID_ARG"
+        return
     rng = np.random.default_rng(m * 7 + n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
     wq = rng.integers(-127, 128, (n, k)).astype(np.int8)
@@ -323,10 +331,12 @@ def test_per_channel_square_weight_decodes_rows_not_columns(g):
     assert np.array_equal(oracle.bf16_to_f64(w_hat), w.astype(np.float64))
 
 
-@pytest.mark.parametrize("tile", [0, 128, 192, 256])
-@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (255, 16, 192), (257, 272, 320), (33, 1040, 64),
-                                   (400, 592, 384), (300, 400, 1152), (300, 400, 1088)])
+@pytest.mark.parametrize("tile", [0, 128, 192, 256, 384])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (255, 16, 192), (257, 272, 320), (33, 1040, 64),
+                                   (400, 592, 384), (300, 400, 1152), (800, 208, 256)])
 def test_per_channel_gemm_shapes(m, n, k, tile):
+    if tile == 384 and k % 128:
+        pytest.skip("the 384 x 192 tile needs K % 128 == 0")
     _announce(f"per-channel gemm shape {m}x{n}x{k} tile={tile}")
     rng = np.random.default_rng(m * 5 + n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
@@ -434,9 +444,11 @@ def test_f16_edge_rows(g):
 
 
 @pytest.mark.parametrize("per_channel", [False, True])
-@pytest.mark.parametrize("tile", [0, 128, 192, 256])
+@pytest.mark.parametrize("tile", [0, 128, 192, 256, 384])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (257, 272, 320), (300, 400, 1152)])
 def test_f16_gemm_shapes(m, n, k, tile, per_channel):
+    if tile == 384 and k % 128:
+        pytest.skip("the 384 x 192 tile needs K % 128 == 0")
     _announce(f"f16 gemm {m}x{n}x{k} tile={tile} pc={per_channel}")
     rng = np.random.default_rng(m + 3 * n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)

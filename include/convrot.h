@@ -49,7 +49,9 @@
  *     last axis is K (input features). bf16 tensors are passed as uint16_t*.
  *     Scales (s_w, s_x) live in device memory too.
  *   - The caller owns every buffer. The library allocates and frees nothing
- *     and keeps no state between calls (apart from a per-thread error string).
+ *     and keeps no state between calls (apart from a per-thread error string),
+ *     except for the convrot_streamer object below, which owns its staging
+ *     memory, copy stream and events from create to destroy.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; the library never synchronizes. The
  *     return value covers argument checks and launch errors; a fault inside a
@@ -74,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 3
+#define CONVROT_ABI_VERSION 4
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -228,6 +230,37 @@ convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const flo
                                       int64_t n, int64_t k, int g, uint64_t rot_seed, void* y,
                                       convrot_dtype dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/* Host-streamed int8 layers (Invoke docs "int8 Compute": a layer still in
+ * system RAM is copied to the GPU as int8 for each step, half the bytes of the
+ * unpacked weight, and computed exactly like a resident one; "Memory": the
+ * copy stays within the default path's working memory).
+ *
+ * A convrot_streamer owns `slots` device staging buffers of slot_bytes each, a
+ * copy stream of its own (default priority) and two events per slot; it is
+ * the one object of this library that allocates (at create; destroy frees).
+ * convrot_streamer_linear_int8 is convrot_linear_int8_ex with the weight wq_host
+ * in host memory (pinned, from hipHostMalloc, for the copy to run
+ * asynchronously; device memory also works): it copies the weight into the
+ * next slot on the copy stream (after that slot's previous forward has
+ * finished), makes `stream` wait for the copy, and enqueues the forward
+ * reading the slot. Calls return at once, so the copies of later layers
+ * overlap the forwards of earlier ones; the output is bit-identical to
+ * convrot_linear_int8_ex on a resident copy of the weight. wq_host must stay
+ * unchanged until the forward that reads it has finished. A streamer is used
+ * by one host thread at a time, on the device current at create. Errors as
+ * for convrot_linear_int8_ex, plus CONVROT_E_WORKSPACE when n*k exceeds
+ * slot_bytes; a HIP error after the copy was enqueued may leave it enqueued. */
+#define CONVROT_STREAMER_MAX_SLOTS 8
+typedef struct convrot_streamer convrot_streamer;
+convrot_status convrot_streamer_create(size_t slot_bytes, int slots, convrot_streamer** out);
+convrot_status convrot_streamer_destroy(convrot_streamer* streamer);
+convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const void* x,
+                                            convrot_dtype dtype, const int8_t* wq_host,
+                                            const float* s_w, convrot_scale_mode scale_mode,
+                                            const void* bias, int64_t m, int64_t n, int64_t k,
+                                            int g, uint64_t rot_seed, void* y, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);

@@ -24,7 +24,8 @@ __all__ = [
     "convrot_quantize_weights_per_channel", "convrot_dequant_derotate_per_channel",
     "convrot_gemm_int8_per_channel", "convrot_linear_int8_per_channel",
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
-    "convrot_linear_int8_ex", "EXPORTED_SYMBOLS",
+    "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
+    "convrot_streamer_linear_int8", "Streamer", "EXPORTED_SYMBOLS",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -44,7 +45,8 @@ EXPORTED_SYMBOLS = (
     "convrot_gemm_int8_per_channel", "convrot_gemm_int8_per_channel_tile",
     "convrot_linear_int8_per_channel",
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
-    "convrot_linear_int8_ex",
+    "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
+    "convrot_streamer_linear_int8",
 )
 
 # convrot_dtype and convrot_scale_mode values
@@ -100,6 +102,10 @@ def load_library():
             "convrot_dequant_derotate_ex": [P, P, I, I64, I64, I, U64, P, I, P],
             "convrot_gemm_int8_ex": [P, P, P, P, I, P, I64, I64, I64, P, P, I, I, P],
             "convrot_linear_int8_ex": [P, P, P, I, P, I64, I64, I64, I, U64, P, I, P, SZ, P],
+            "convrot_streamer_create": [SZ, I, ctypes.POINTER(P)],
+            "convrot_streamer_destroy": [P],
+            "convrot_streamer_linear_int8": [P, P, I, P, P, I, P, I64, I64, I64, I, U64, P, P, SZ,
+                                             P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -453,3 +459,73 @@ def convrot_linear_int8_ex(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
                                                  _ptr(workspace), workspace.numel(),
                                                  _stream(x)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Host-streamed int8 layers
+# ---------------------------------------------------------------------------
+
+def convrot_streamer_create(slot_bytes: int, slots: int = 2) -> ctypes.c_void_p:
+    """A streamer with `slots` device staging buffers of slot_bytes each, on
+    the current device. Free it with convrot_streamer_destroy."""
+    h = ctypes.c_void_p()
+    _check(load_library().convrot_streamer_create(slot_bytes, slots, ctypes.byref(h)))
+    return h
+
+
+def convrot_streamer_destroy(streamer: ctypes.c_void_p) -> None:
+    _check(load_library().convrot_streamer_destroy(streamer))
+
+
+def convrot_streamer_linear_int8(streamer: ctypes.c_void_p, x: torch.Tensor,
+                                 wq_host: torch.Tensor, s_w: torch.Tensor, g: int,
+                                 rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                                 per_channel: bool = False, workspace: torch.Tensor | None = None,
+                                 out: torch.Tensor | None = None):
+    """convrot_linear_int8_ex with the int8 weight in host memory (pinned for
+    an asynchronous copy): copied into the streamer's next slot, then used."""
+    dt = _need16(x, "x", 2)
+    if not isinstance(wq_host, torch.Tensor) or wq_host.dtype != torch.int8 or wq_host.dim() != 2:
+        raise TypeError("wq_host must be a 2-D int8 tensor")
+    if not wq_host.is_contiguous():
+        raise ValueError("wq_host must be contiguous")
+    m, k = x.shape
+    n = wq_host.shape[0]
+    if wq_host.shape[1] != k:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs wq_host {tuple(wq_host.shape)}")
+    _need_sw(s_w, per_channel, n)
+    if bias is not None:
+        _need(bias, "bias", x.dtype, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_int8_workspace_size(m, n, k), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    out = torch.empty((m, n), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out", x.dtype, 2)
+    _same_device(x, s_w, bias, workspace, out)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_streamer_linear_int8(
+        streamer, _ptr(x), dt, _ptr(wq_host), _ptr(s_w), mode, _ptr(bias), m, n, k, g, rot_seed,
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+class Streamer:
+    """Owns a convrot_streamer: `with Streamer(slot_bytes) as s: s.linear(...)`."""
+
+    def __init__(self, slot_bytes: int, slots: int = 2):
+        self.handle = convrot_streamer_create(slot_bytes, slots)
+
+    def linear(self, x, wq_host, s_w, g, rot_seed=ROT_SEED, bias=None, **kw):
+        return convrot_streamer_linear_int8(self.handle, x, wq_host, s_w, g, rot_seed, bias, **kw)
+
+    def close(self):
+        if self.handle is not None:
+            convrot_streamer_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -360,11 +360,13 @@ size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k) {
   return convrot_linear_int8_workspace_for_rows(rows, k);
 }
 
-static convrot_status linear_impl(const char* fn, bool pc, DType dt, const uint16_t* x,
-                                  const int8_t* wq,
-                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
-                                  int64_t k, int g, uint64_t rot_seed, uint16_t* y,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks of the int8_compute forward; on success *slice holds the
+// token rows per slice (0 when m == 0: nothing to do).
+static convrot_status linear_check(const char* fn, bool pc, const uint16_t* x, const int8_t* wq,
+                                   const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
+                                   int64_t k, int g, const uint16_t* y, const void* workspace,
+                                   size_t workspace_bytes, int64_t* slice) {
+  *slice = 0;
   if (!wq || !s_w) return fail(CONVROT_E_INVALID_ARG, "%s: null pointer", fn);
   if (convrot_status s = check_rot(fn, m, k, g)) return s;
   if (convrot_status s = check_gemm(fn, m, n, k)) return s;
@@ -387,10 +389,17 @@ static convrot_status linear_impl(const char* fn, bool pc, DType dt, const uint1
       overlap(workspace, workspace_bytes, wq, (size_t)(n * k)) ||
       overlap(y, ny, s_w, sw_bytes(pc, n)) || overlap(workspace, workspace_bytes, s_w, sw_bytes(pc, n)))
     return fail(CONVROT_E_INVALID_ARG, "%s: overlapping buffers", fn);
-  if (m == 0) return ok();
   // whole GEMM tiles per slice when the workspace allows
-  int64_t slice = rows_fit < m ? rows_fit : m;
-  if (slice < m && slice >= 256) slice -= slice % 256;
+  *slice = rows_fit < m ? rows_fit : m;
+  if (*slice < m && *slice >= 256) *slice -= *slice % 256;
+  return ok();
+}
+
+// Launches of the int8_compute forward (arguments already checked).
+static convrot_status linear_run(const char* fn, bool pc, DType dt, const uint16_t* x,
+                                 const int8_t* wq, const float* s_w, const uint16_t* bias,
+                                 int64_t m, int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                 uint16_t* y, void* workspace, int64_t slice, void* stream) {
   const SignMask sm = make_signs(rot_seed, g);
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
@@ -404,6 +413,20 @@ static convrot_status linear_impl(const char* fn, bool pc, DType dt, const uint1
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+static convrot_status linear_impl(const char* fn, bool pc, DType dt, const uint16_t* x,
+                                  const int8_t* wq, const float* s_w, const uint16_t* bias,
+                                  int64_t m, int64_t n, int64_t k, int g, uint64_t rot_seed,
+                                  uint16_t* y, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  int64_t slice;
+  if (convrot_status s = linear_check(fn, pc, x, wq, s_w, bias, m, n, k, g, y, workspace,
+                                      workspace_bytes, &slice))
+    return s;
+  if (slice == 0) return ok();
+  return linear_run(fn, pc, dt, x, wq, s_w, bias, m, n, k, g, rot_seed, y, workspace, slice,
+                    stream);
 }
 
 convrot_status convrot_linear_int8(const uint16_t* x, const int8_t* wq, const float* s_w,
@@ -437,6 +460,115 @@ convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const flo
   return linear_impl(fn, pc, dt, static_cast<const uint16_t*>(x), wq, s_w,
                      static_cast<const uint16_t*>(bias), m, n, k, g, rot_seed,
                      static_cast<uint16_t*>(y), workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Host-streamed int8 layers: a ring of device staging slots. Each call copies
+// one layer's int8 weight into the next slot on the streamer's own copy
+// stream, and the forward waits for that copy on the caller's stream; the
+// next call's copy waits only for its own slot's previous forward, so the
+// copies of later layers overlap the forwards of earlier ones.
+// ---------------------------------------------------------------------------
+
+struct convrot_streamer {
+  int device;
+  size_t slot_bytes;
+  int nslots;
+  int next;
+  void* slot[CONVROT_STREAMER_MAX_SLOTS];
+  hipEvent_t ready[CONVROT_STREAMER_MAX_SLOTS];     // the slot's copy is done
+  hipEvent_t released[CONVROT_STREAMER_MAX_SLOTS];  // the slot's forward is done
+  hipStream_t copy;
+};
+
+static void streamer_release(convrot_streamer* s) {
+  if (s->copy) (void)hipStreamSynchronize(s->copy);
+  for (int i = 0; i < s->nslots; ++i) {
+    if (s->released[i]) (void)hipEventSynchronize(s->released[i]);
+    if (s->slot[i]) (void)hipFree(s->slot[i]);
+    if (s->ready[i]) (void)hipEventDestroy(s->ready[i]);
+    if (s->released[i]) (void)hipEventDestroy(s->released[i]);
+  }
+  if (s->copy) (void)hipStreamDestroy(s->copy);
+  delete s;
+}
+
+convrot_status convrot_streamer_create(size_t slot_bytes, int slots, convrot_streamer** out) {
+  const char* fn = "convrot_streamer_create";
+  if (!out) return fail(CONVROT_E_INVALID_ARG, "%s: null output", fn);
+  *out = nullptr;
+  if (slots < 1 || slots > CONVROT_STREAMER_MAX_SLOTS || slot_bytes == 0)
+    return fail(CONVROT_E_INVALID_ARG, "%s: slots=%d (1..%d), slot_bytes=%zu", fn, slots,
+                CONVROT_STREAMER_MAX_SLOTS, slot_bytes);
+  convrot_streamer* s = new convrot_streamer();
+  s->slot_bytes = slot_bytes;
+  s->nslots = slots;
+  hipError_t e = hipGetDevice(&s->device);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&s->copy, hipStreamNonBlocking);
+  for (int i = 0; i < slots && e == hipSuccess; ++i) {
+    e = hipMalloc(&s->slot[i], align_up(slot_bytes, 256));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s->ready[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s->released[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    streamer_release(s);
+    return hip_status(e, fn);
+  }
+  *out = s;
+  return ok();
+}
+
+convrot_status convrot_streamer_destroy(convrot_streamer* s) {
+  if (!s) return fail(CONVROT_E_INVALID_ARG, "convrot_streamer_destroy: null streamer");
+  streamer_release(s);
+  return ok();
+}
+
+convrot_status convrot_streamer_linear_int8(convrot_streamer* s, const void* x, convrot_dtype dtype,
+                                            const int8_t* wq_host, const float* s_w,
+                                            convrot_scale_mode scale_mode, const void* bias,
+                                            int64_t m, int64_t n, int64_t k, int g,
+                                            uint64_t rot_seed, void* y, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const char* fn = "convrot_streamer_linear_int8";
+  bool pc;
+  DType dt;
+  if (!s) return fail(CONVROT_E_INVALID_ARG, "%s: null streamer", fn);
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  if (!wq_host) return fail(CONVROT_E_INVALID_ARG, "%s: null weight", fn);
+  if (n > 0 && k > 0 && (size_t)n * (size_t)k > s->slot_bytes)
+    return fail(CONVROT_E_WORKSPACE, "%s: weight of %lld bytes exceeds the %zu-byte slots", fn,
+                (long long)(n * k), s->slot_bytes);
+  const int i = s->next;
+  const int8_t* wq = static_cast<const int8_t*>(s->slot[i]);
+  int64_t slice;
+  if (convrot_status st = linear_check(fn, pc, static_cast<const uint16_t*>(x), wq, s_w,
+                                       static_cast<const uint16_t*>(bias), m, n, k, g,
+                                       static_cast<const uint16_t*>(y), workspace,
+                                       workspace_bytes, &slice))
+    return st;
+  if (slice == 0) return ok();
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev != s->device)
+    return fail(CONVROT_E_INVALID_ARG, "%s: current device %d, streamer made on device %d", fn,
+                dev, s->device);
+  hipStream_t st = (hipStream_t)stream;
+  e = hipStreamWaitEvent(s->copy, s->released[i], 0);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(s->slot[i], wq_host, (size_t)(n * k), hipMemcpyDefault, s->copy);
+  if (e == hipSuccess) e = hipEventRecord(s->ready[i], s->copy);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, s->ready[i], 0);
+  if (e != hipSuccess) return hip_status(e, fn);
+  s->next = (i + 1) % s->nslots;
+  if (convrot_status r = linear_run(fn, pc, dt, static_cast<const uint16_t*>(x), wq, s_w,
+                                    static_cast<const uint16_t*>(bias), m, n, k, g, rot_seed,
+                                    static_cast<uint16_t*>(y), workspace, slice, stream))
+    return r;
+  return hip_status(hipEventRecord(s->released[i], st), fn);
 }
 
 }  // extern "C"

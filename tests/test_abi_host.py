@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 3
+    assert cr.convrot_abi_version() == 4
     for s in range(7):
         assert cr.convrot_status_string(s)
 
@@ -208,3 +208,15 @@ def test_ex_entry_points_reject_unknown_enums(lib):
     assert _status(lib, "convrot_linear_int8_ex", FAKE, ctypes.c_void_p(1 << 24),
                    ctypes.c_void_p(1 << 26), 0, None, 0, n, k, 256, 1, ctypes.c_void_p(1 << 28),
                    1, ctypes.c_void_p(1 << 32), 1 << 20, None) == 0
+
+
+def test_streamer_argument_checks_without_gpu(lib):
+    """rejected before any HIP call: a null streamer or output, bad slot counts"""
+    h = ctypes.c_void_p()
+    assert lib.convrot_streamer_create(1 << 20, 0, ctypes.byref(h)) == 1
+    assert lib.convrot_streamer_create(1 << 20, 9, ctypes.byref(h)) == 1
+    assert lib.convrot_streamer_create(0, 2, ctypes.byref(h)) == 1
+    assert lib.convrot_streamer_create(1 << 20, 2, None) == 1
+    assert lib.convrot_streamer_destroy(None) == 1
+    assert lib.convrot_streamer_linear_int8(None, FAKE, 0, FAKE, FAKE, 0, None, 8, 64, 256, 256, 1,
+                                            FAKE, FAKE, 1 << 20, None) == 1

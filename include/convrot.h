@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 4
+#define CONVROT_ABI_VERSION 5
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -85,7 +85,8 @@ typedef enum convrot_status {
   CONVROT_E_UNSUPPORTED_SHAPE = 3, /* a shape limit above is not met                          */
   CONVROT_E_MISALIGNED = 4,        /* a pointer is not aligned as required                    */
   CONVROT_E_WORKSPACE = 5,         /* workspace too small for one token row                   */
-  CONVROT_E_HIP = 6                /* a HIP call failed; see convrot_last_error_string()      */
+  CONVROT_E_HIP = 6,               /* a HIP call failed; see convrot_last_error_string()      */
+  CONVROT_E_SELFCHECK = 7          /* a session's first-call check failed (latched)           */
 } convrot_status;
 
 /* 16-bit float format of activations, bias, outputs and W_hat (the *_ex
@@ -261,6 +262,50 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const vo
                                             const void* bias, int64_t m, int64_t n, int64_t k,
                                             int g, uint64_t rot_seed, void* y, void* workspace,
                                             size_t workspace_bytes, void* stream);
+
+/* First-call tuning and self-check (Invoke docs "int8 Compute", "Memory" and
+ * "When something goes wrong": the first call for each layer shape and
+ * token-count bucket tunes the kernels with a cache-sized buffer and is
+ * checked against the default path on 256 output rows; on a mismatch or a
+ * failing kernel that GPU keeps the default path until restart).
+ *
+ * A convrot_session (one per device, made on the current device) runs
+ * convrot_linear_int8_ex through a table keyed by (n, k, token bucket, g,
+ * dtype, scale_mode), the token bucket being ceil(log2 m). On the first call
+ * for a key, synchronously on `stream`:
+ *   1. the first token slice is quantized and every GEMM tile that exists
+ *      for k is timed on it (two runs each, after 256 MB - the MI355X MALL -
+ *      have been written to a temporary buffer); the fastest is kept;
+ *   2. the forward runs with that tile and writes y;
+ *   3. W_hat (convrot_dequant_derotate_ex in dtype) is formed in a temporary
+ *      buffer, the first min(m, 256) rows of x . W_hat^T (+ bias) are computed
+ *      in fp32, and their relative Frobenius distance e from the same rows of
+ *      y is kept. e <= check_tolerance passes.
+ * Later calls for the key run the forward with the kept tile and enqueue
+ * asynchronously, like convrot_linear_int8_ex (same results: every tile gives
+ * the same bits). If the check fails, or a HIP call of a first call fails,
+ * the session latches: that call (which has written y) and every later call
+ * return CONVROT_E_SELFCHECK (later calls enqueue nothing), and the caller takes the
+ * default path (convrot_dequant_derotate_ex and its own bf16 / fp16 matmul).
+ * The library never switches paths silently. The quantization noise of the
+ * int8 path is a few percent at most (per-token int8 after the rotation);
+ * check_tolerance <= 0 selects 0.1. First calls allocate and free temporary
+ * device memory (256 MB + 2nk + 1 KB per row of n outputs). A session is
+ * safe to share between threads (calls are serialized). */
+typedef struct convrot_session convrot_session;
+convrot_status convrot_session_create(double check_tolerance, convrot_session** out);
+convrot_status convrot_session_destroy(convrot_session* session);
+convrot_status convrot_session_linear_int8(convrot_session* session, const void* x,
+                                           convrot_dtype dtype, const int8_t* wq,
+                                           const float* s_w, convrot_scale_mode scale_mode,
+                                           const void* bias, int64_t m, int64_t n, int64_t k,
+                                           int g, uint64_t rot_seed, void* y, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+/* The tile kept for a key and the check's relative error e; CONVROT_E_INVALID_ARG
+ * if the key has had no first call. *latched (nullable) reports the latch. */
+convrot_status convrot_session_lookup(convrot_session* session, int64_t m, int64_t n, int64_t k,
+                                      int g, convrot_dtype dtype, convrot_scale_mode scale_mode,
+                                      int* tile, double* check_error, int* latched);
 
 /* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);

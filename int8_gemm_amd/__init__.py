@@ -25,7 +25,9 @@ __all__ = [
     "convrot_gemm_int8_per_channel", "convrot_linear_int8_per_channel",
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
-    "convrot_streamer_linear_int8", "Streamer", "EXPORTED_SYMBOLS",
+    "convrot_streamer_linear_int8", "Streamer", "convrot_session_create",
+    "convrot_session_destroy", "convrot_session_linear_int8", "convrot_session_lookup",
+    "Session", "EXPORTED_SYMBOLS",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -46,7 +48,8 @@ EXPORTED_SYMBOLS = (
     "convrot_linear_int8_per_channel",
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
-    "convrot_streamer_linear_int8",
+    "convrot_streamer_linear_int8", "convrot_session_create", "convrot_session_destroy",
+    "convrot_session_linear_int8", "convrot_session_lookup",
 )
 
 # convrot_dtype and convrot_scale_mode values
@@ -55,7 +58,7 @@ _SCALE_PER_TENSOR, _SCALE_PER_CHANNEL = 0, 1
 
 _STATUS = {0: "CONVROT_OK", 1: "CONVROT_E_INVALID_ARG", 2: "CONVROT_E_UNSUPPORTED_GROUP",
            3: "CONVROT_E_UNSUPPORTED_SHAPE", 4: "CONVROT_E_MISALIGNED", 5: "CONVROT_E_WORKSPACE",
-           6: "CONVROT_E_HIP"}
+           6: "CONVROT_E_HIP", 7: "CONVROT_E_SELFCHECK"}
 
 
 class ConvrotError(RuntimeError):
@@ -106,6 +109,12 @@ def load_library():
             "convrot_streamer_destroy": [P],
             "convrot_streamer_linear_int8": [P, P, I, P, P, I, P, I64, I64, I64, I, U64, P, P, SZ,
                                              P],
+            "convrot_session_create": [ctypes.c_double, ctypes.POINTER(P)],
+            "convrot_session_destroy": [P],
+            "convrot_session_linear_int8": [P, P, I, P, P, I, P, I64, I64, I64, I, U64, P, P, SZ,
+                                            P],
+            "convrot_session_lookup": [P, I64, I64, I64, I, I, I, ctypes.POINTER(I),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -522,6 +531,87 @@ class Streamer:
     def close(self):
         if self.handle is not None:
             convrot_streamer_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+# ---------------------------------------------------------------------------
+# Sessions: first-call tile tuning and check against the default path
+# ---------------------------------------------------------------------------
+
+def convrot_session_create(check_tolerance: float = 0.0) -> ctypes.c_void_p:
+    """A session on the current device (check_tolerance <= 0: 0.1)."""
+    h = ctypes.c_void_p()
+    _check(load_library().convrot_session_create(check_tolerance, ctypes.byref(h)))
+    return h
+
+
+def convrot_session_destroy(session: ctypes.c_void_p) -> None:
+    _check(load_library().convrot_session_destroy(session))
+
+
+def convrot_session_linear_int8(session: ctypes.c_void_p, x: torch.Tensor, wq: torch.Tensor,
+                                s_w: torch.Tensor, g: int, rot_seed: int = ROT_SEED,
+                                bias: torch.Tensor | None = None, *, per_channel: bool = False,
+                                workspace: torch.Tensor | None = None,
+                                out: torch.Tensor | None = None):
+    """convrot_linear_int8_ex through a session: the first call for each
+    (shape, token bucket) tunes the GEMM tile and checks the result against
+    the default path; a failed check raises ConvrotError (CONVROT_E_SELFCHECK)
+    now and on every later call."""
+    dt = _need16(x, "x", 2)
+    _need(wq, "wq", torch.int8, 2)
+    m, k = x.shape
+    n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
+    if bias is not None:
+        _need(bias, "bias", x.dtype, 1)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_int8_workspace_size(m, n, k), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    out = torch.empty((m, n), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out", x.dtype, 2)
+    _same_device(x, wq, s_w, bias, workspace, out)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_session_linear_int8(
+        session, _ptr(x), dt, _ptr(wq), _ptr(s_w), mode, _ptr(bias), m, n, k, g, rot_seed,
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+def convrot_session_lookup(session: ctypes.c_void_p, m: int, n: int, k: int, g: int,
+                           dtype: torch.dtype = torch.bfloat16, per_channel: bool = False):
+    """(tile, check_error, latched) kept for a key; ConvrotError if the key
+    has had no first call."""
+    tile, err, latched = ctypes.c_int(), ctypes.c_double(), ctypes.c_int()
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_session_lookup(session, m, n, k, g, _DTYPES[dtype], mode,
+                                                 ctypes.byref(tile), ctypes.byref(err),
+                                                 ctypes.byref(latched)))
+    return tile.value, err.value, bool(latched.value)
+
+
+class Session:
+    """Owns a convrot_session: `with Session() as s: s.linear(...)`."""
+
+    def __init__(self, check_tolerance: float = 0.0):
+        self.handle = convrot_session_create(check_tolerance)
+
+    def linear(self, x, wq, s_w, g, rot_seed=ROT_SEED, bias=None, **kw):
+        return convrot_session_linear_int8(self.handle, x, wq, s_w, g, rot_seed, bias, **kw)
+
+    def lookup(self, m, n, k, g, dtype=torch.bfloat16, per_channel=False):
+        return convrot_session_lookup(self.handle, m, n, k, g, dtype, per_channel)
+
+    def close(self):
+        if self.handle is not None:
+            convrot_session_destroy(self.handle)
             self.handle = None
 
     def __enter__(self):

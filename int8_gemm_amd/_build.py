@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ("api.hip", "rotate.hip", "dequant.hip", "gemm.hip")
+SOURCES = ("api.hip", "rotate.hip", "dequant.hip", "gemm.hip", "check.hip")
 
 # -ffp-contract=off: the numerics contract spells out every fp32 rounding; a
 # fused multiply-add would skip one. The packed-fp32 feature is turned off for

@@ -7,7 +7,12 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
+#include <map>
 #include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
 
 #include "../../include/convrot.h"
 #include "common.h"
@@ -134,6 +139,7 @@ const char* convrot_status_string(convrot_status s) {
     case CONVROT_E_MISALIGNED: return "misaligned pointer";
     case CONVROT_E_WORKSPACE: return "workspace too small";
     case CONVROT_E_HIP: return "HIP error";
+    case CONVROT_E_SELFCHECK: return "first-call check failed (latched)";
   }
   return "unknown status";
 }
@@ -395,11 +401,13 @@ static convrot_status linear_check(const char* fn, bool pc, const uint16_t* x, c
   return ok();
 }
 
-// Launches of the int8_compute forward (arguments already checked).
+// Launches of the int8_compute forward (arguments already checked); tile 0
+// lets the GEMM choose its block tile.
 static convrot_status linear_run(const char* fn, bool pc, DType dt, const uint16_t* x,
                                  const int8_t* wq, const float* s_w, const uint16_t* bias,
                                  int64_t m, int64_t n, int64_t k, int g, uint64_t rot_seed,
-                                 uint16_t* y, void* workspace, int64_t slice, void* stream) {
+                                 uint16_t* y, void* workspace, int64_t slice, void* stream,
+                                 int tile = 0) {
   const SignMask sm = make_signs(rot_seed, g);
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
@@ -409,7 +417,8 @@ static convrot_status linear_run(const char* fn, bool pc, DType dt, const uint16
     const int64_t rows = (m - r0) < slice ? (m - r0) : slice;
     hipError_t e = launch_quantize_rows(x + r0 * k, xq, sx, rows, (int)k, g, sm, dt, st);
     if (e != hipSuccess) return hip_status(e, fn);
-    e = launch_gemm(xq, sx, wq, s_w, pc, bias, rows, n, k, y + r0 * n, nullptr, dt, st);
+    e = launch_gemm_tile(xq, sx, wq, s_w, pc, bias, rows, n, k, y + r0 * n, nullptr, tile, dt,
+                         st);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
@@ -569,6 +578,226 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* s, const void* x, 
                                     static_cast<uint16_t*>(y), workspace, slice, stream))
     return r;
   return hip_status(hipEventRecord(s->released[i], st), fn);
+}
+
+// ---------------------------------------------------------------------------
+// Sessions: first-call tile tuning and check against the default path.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kFlushBytes = (size_t)256 << 20;  // MI355X MALL
+constexpr int kCheckRows = 256;
+
+struct SessionEntry {
+  int tile;
+  double err;
+};
+
+using SessionKey = std::tuple<int64_t, int64_t, int, int, int, int>;
+
+int token_bucket(int64_t m) {
+  int b = 0;
+  while (b < 62 && ((int64_t)1 << b) < m) ++b;
+  return b;  // ceil(log2 m)
+}
+
+// device buffers freed on scope exit
+struct DeviceTemp {
+  void* p = nullptr;
+  hipError_t alloc(size_t bytes) { return hipMalloc(&p, bytes); }
+  ~DeviceTemp() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+}  // namespace
+
+struct convrot_session {
+  int device = -1;
+  double tol = 0.1;
+  bool latched = false;
+  std::string latch_reason;
+  std::map<SessionKey, SessionEntry> entries;
+  std::mutex mu;
+};
+
+convrot_status convrot_session_create(double check_tolerance, convrot_session** out) {
+  const char* fn = "convrot_session_create";
+  if (!out) return fail(CONVROT_E_INVALID_ARG, "%s: null output", fn);
+  *out = nullptr;
+  if (std::isnan(check_tolerance))
+    return fail(CONVROT_E_INVALID_ARG, "%s: tolerance is NaN", fn);
+  convrot_session* s = new convrot_session();
+  s->tol = check_tolerance > 0 ? check_tolerance : 0.1;
+  const hipError_t e = hipGetDevice(&s->device);
+  if (e != hipSuccess) {
+    delete s;
+    return hip_status(e, fn);
+  }
+  *out = s;
+  return ok();
+}
+
+convrot_status convrot_session_destroy(convrot_session* s) {
+  if (!s) return fail(CONVROT_E_INVALID_ARG, "convrot_session_destroy: null session");
+  delete s;
+  return ok();
+}
+
+// The first call for a key: tune, run, check. Returns the status; on success
+// *entry holds the kept tile and the check's error.
+static convrot_status session_first_call(const char* fn, convrot_session* s, bool pc, DType dt,
+                                         const uint16_t* x, const int8_t* wq, const float* s_w,
+                                         const uint16_t* bias, int64_t m, int64_t n, int64_t k,
+                                         int g, uint64_t rot_seed, uint16_t* y, void* workspace,
+                                         int64_t slice, hipStream_t st, SessionEntry* entry) {
+  const SignMask sm = make_signs(rot_seed, g);
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       align_up((size_t)(slice * k), 256));
+  const int64_t rows0 = slice < m ? slice : m;
+  hipError_t e = launch_quantize_rows(x, xq, sx, rows0, (int)k, g, sm, dt, st);
+  // 1. time every tile that exists for k on the first slice, caches flushed
+  int best = 0;
+  float best_ms = 0.0f;
+  {
+    DeviceTemp flush;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (e == hipSuccess) e = flush.alloc(kFlushBytes);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    const int cands[] = {384, 256, 192, 128};
+    for (int c : cands) {
+      if (e != hipSuccess) break;
+      if (c == 384 && k % 128 != 0) continue;
+      for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+        e = launch_flush(flush.p, kFlushBytes, st);
+        if (e == hipSuccess) e = hipEventRecord(e0, st);
+        if (e == hipSuccess)
+          e = launch_gemm_tile(xq, sx, wq, s_w, pc, bias, rows0, n, k, y, nullptr, c, dt, st);
+        if (e == hipSuccess) e = hipEventRecord(e1, st);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e == hipSuccess && (best == 0 || ms < best_ms)) {
+          best = c;
+          best_ms = ms;
+        }
+      }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+  }
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 2. the forward with the kept tile
+  if (convrot_status r = linear_run(fn, pc, dt, x, wq, s_w, bias, m, n, k, g, rot_seed, y,
+                                    workspace, slice, st, best))
+    return r;
+  // 3. the check against the default path on the first rows
+  const int rows = (int)(m < kCheckRows ? m : kCheckRows);
+  DeviceTemp w_hat, y_ref, partial;
+  e = w_hat.alloc((size_t)(n * k) * 2);
+  if (e == hipSuccess) e = y_ref.alloc((size_t)rows * (size_t)n * 4);
+  if (e == hipSuccess) e = partial.alloc((size_t)rows * 2 * sizeof(double));
+  if (e == hipSuccess)
+    e = launch_dequant(wq, s_w, pc, n, k, g, sm, static_cast<uint16_t*>(w_hat.p), dt, st);
+  if (e == hipSuccess)
+    e = launch_check_rows(x, static_cast<const uint16_t*>(w_hat.p), bias, y, rows, (int)n, (int)k,
+                          dt, static_cast<float*>(y_ref.p), static_cast<double*>(partial.p), st);
+  std::vector<double> host((size_t)rows * 2);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host.data(), partial.p, host.size() * sizeof(double),
+                       hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  double d2 = 0.0, r2 = 0.0;
+  for (int r = 0; r < rows; ++r) {
+    d2 += host[2 * r];
+    r2 += host[2 * r + 1];
+  }
+  entry->tile = best;
+  entry->err = r2 > 0.0 ? std::sqrt(d2 / r2) : (d2 == 0.0 ? 0.0 : INFINITY);
+  return ok();
+}
+
+convrot_status convrot_session_linear_int8(convrot_session* s, const void* x, convrot_dtype dtype,
+                                           const int8_t* wq, const float* s_w,
+                                           convrot_scale_mode scale_mode, const void* bias,
+                                           int64_t m, int64_t n, int64_t k, int g,
+                                           uint64_t rot_seed, void* y, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  const char* fn = "convrot_session_linear_int8";
+  bool pc;
+  DType dt;
+  if (!s) return fail(CONVROT_E_INVALID_ARG, "%s: null session", fn);
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  std::lock_guard<std::mutex> lock(s->mu);
+  if (s->latched)
+    return fail(CONVROT_E_SELFCHECK, "%s: latched (%s); use the default path", fn,
+                s->latch_reason.c_str());
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* bb = static_cast<const uint16_t*>(bias);
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  int64_t slice;
+  if (convrot_status st = linear_check(fn, pc, xb, wq, s_w, bb, m, n, k, g, yb, workspace,
+                                       workspace_bytes, &slice))
+    return st;
+  if (slice == 0) return ok();
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev != s->device)
+    return fail(CONVROT_E_INVALID_ARG, "%s: current device %d, session made on device %d", fn,
+                dev, s->device);
+  const SessionKey key{n, k, token_bucket(m), g, (int)dt, pc ? 1 : 0};
+  auto it = s->entries.find(key);
+  if (it != s->entries.end())
+    return linear_run(fn, pc, dt, xb, wq, s_w, bb, m, n, k, g, rot_seed, yb, workspace, slice,
+                      stream, it->second.tile);
+  SessionEntry entry{0, 0.0};
+  const convrot_status r = session_first_call(fn, s, pc, dt, xb, wq, s_w, bb, m, n, k, g, rot_seed,
+                                              yb, workspace, slice, (hipStream_t)stream, &entry);
+  char why[256];
+  if (r != CONVROT_OK) {
+    snprintf(why, sizeof why, "first call for n=%lld k=%lld failed: %s", (long long)n,
+             (long long)k, g_last_error);
+    s->latched = true;
+    s->latch_reason = why;
+    return fail(CONVROT_E_SELFCHECK, "%s: %s", fn, why);
+  }
+  s->entries[key] = entry;
+  if (!(entry.err <= s->tol)) {
+    snprintf(why, sizeof why,
+             "first result for n=%lld k=%lld (token bucket 2^%d) is %.4g away from the default "
+             "path, tolerance %.4g",
+             (long long)n, (long long)k, token_bucket(m), entry.err, s->tol);
+    s->latched = true;
+    s->latch_reason = why;
+    return fail(CONVROT_E_SELFCHECK, "%s: %s", fn, why);
+  }
+  return ok();
+}
+
+convrot_status convrot_session_lookup(convrot_session* s, int64_t m, int64_t n, int64_t k, int g,
+                                      convrot_dtype dtype, convrot_scale_mode scale_mode,
+                                      int* tile, double* check_error, int* latched) {
+  const char* fn = "convrot_session_lookup";
+  bool pc;
+  DType dt;
+  if (!s) return fail(CONVROT_E_INVALID_ARG, "%s: null session", fn);
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  std::lock_guard<std::mutex> lock(s->mu);
+  if (latched) *latched = s->latched ? 1 : 0;
+  auto it = s->entries.find(SessionKey{n, k, token_bucket(m), g, (int)dt, pc ? 1 : 0});
+  if (it == s->entries.end()) return fail(CONVROT_E_INVALID_ARG, "%s: no first call yet", fn);
+  if (tile) *tile = it->second.tile;
+  if (check_error) *check_error = it->second.err;
+  return ok();
 }
 
 }  // extern "C"

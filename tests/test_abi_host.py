@@ -45,9 +45,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 4
-    for s in range(7):
+    assert cr.convrot_abi_version() == 5
+    for s in range(8):
         assert cr.convrot_status_string(s)
+    assert cr.convrot_status_string(7).startswith("first-call check")
 
 
 @pytest.mark.parametrize("seed", [synth.ROT_SEED, 0, 1, 2 ** 64 - 1, 0x123456789ABCDEF])
@@ -220,3 +221,15 @@ def test_streamer_argument_checks_without_gpu(lib):
     assert lib.convrot_streamer_destroy(None) == 1
     assert lib.convrot_streamer_linear_int8(None, FAKE, 0, FAKE, FAKE, 0, None, 8, 64, 256, 256, 1,
                                             FAKE, FAKE, 1 << 20, None) == 1
+
+
+def test_session_argument_checks_without_gpu(lib):
+    h = ctypes.c_void_p()
+    assert lib.convrot_session_create(float("nan"), ctypes.byref(h)) == 1
+    assert lib.convrot_session_create(0.1, None) == 1
+    assert lib.convrot_session_destroy(None) == 1
+    assert lib.convrot_session_linear_int8(None, FAKE, 0, FAKE, FAKE, 0, None, 8, 64, 256, 256, 1,
+                                           FAKE, FAKE, 1 << 20, None) == 1
+    t, e, lt = ctypes.c_int(), ctypes.c_double(), ctypes.c_int()
+    assert lib.convrot_session_lookup(None, 8, 64, 256, 256, 0, 0, ctypes.byref(t),
+                                      ctypes.byref(e), ctypes.byref(lt)) == 1

@@ -735,7 +735,10 @@ hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, in
 // costs little on ordinary inputs and keeps the chip busy on inputs (GELU
 // tails) that defer most rows.
 constexpr int kExactWavesPerCU = 8;
-constexpr int kDeferredWavesPerCU = 8;
+#ifndef CONVROT_DEFERRED_WAVES_PER_CU
+#define CONVROT_DEFERRED_WAVES_PER_CU 8
+#endif
+constexpr int kDeferredWavesPerCU = CONVROT_DEFERRED_WAVES_PER_CU;
 
 template <int G>
 hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,

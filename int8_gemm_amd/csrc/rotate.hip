@@ -90,13 +90,6 @@ __device__ __forceinline__ double xor_lanes_f64(double v) {
   return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
-  const uint64_t b = __double_as_longlong(v);
-  const int lo = __shfl_xor((int)(uint32_t)b, m);
-  const int hi = __shfl_xor((int)(uint32_t)(b >> 32), m);
-  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
 // In-lane radix-2 Walsh-Hadamard stages over the low log2(min(G, N)) index
 // bits of v[N]; stage h combines (j, j+h) into (a+b, a-b).
 template <int G, int N>
@@ -420,13 +413,17 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
 #pragma unroll
     for (int i = 0; i < GE / 2; ++i) span_acc(w[gidx * (GE / 2) + i], mx, mn);
     uint32_t a = lane_pack(mx, true), b = lane_pack(mn, false);
-#pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) {
-      const uint32_t ta = (uint32_t)__shfl_xor((int)a, m);
-      const uint32_t tb = (uint32_t)__shfl_xor((int)b, m);
+    // over the LPG lanes of the group (consecutive lanes within 8: DPP)
+    auto xred = [&](auto mt) {
+      constexpr int m = decltype(mt)::value;
+      const uint32_t ta = xor_lanes_u32<m>(a);
+      const uint32_t tb = xor_lanes_u32<m>(b);
       a = a > ta ? a : ta;
       b = b < tb ? b : tb;
-    }
+    };
+    if constexpr (LPG > 1) xred(std::integral_constant<int, 1>{});
+    if constexpr (LPG > 2) xred(std::integral_constant<int, 2>{});
+    if constexpr (LPG > 4) xred(std::integral_constant<int, 4>{});
     const int span = group_span(a, b);
     if (span > 45 - LOGG) gmask |= 1u << gidx;
     int e = (int)(a >> 7);
@@ -434,14 +431,6 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     const int nb = span < 0 ? 0 : span / kBand + 1;
     nb_lane = nb_lane > nb ? nb_lane : nb;
   }
-  // all lanes run the same number of bands (empty bands add nothing)
-  int nb_all = nb_lane;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int t = __shfl_xor(nb_all, m);
-    nb_all = nb_all > t ? nb_all : t;
-  }
-
   if constexpr (WIDE) {
     // ---- one rounded float64 transform first (rows the fast kernel left:
     // mostly wide-span groups). Each output is a depth-LOGG tree of correctly
@@ -565,6 +554,14 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     if (__syncthreads_or(active) == 0) continue;
   }
 
+  // all lanes run the same number of bands (empty bands add nothing)
+  int nb_all = nb_lane;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int t = __shfl_xor(nb_all, m);
+    nb_all = nb_all > t ? nb_all : t;
+  }
+
   double V[CH];
   uint32_t sticky = 0u;
 #pragma unroll
@@ -588,12 +585,16 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
       F[i] = in_band ? (double)xv : 0.0;
     }
     fwht_inlane<G, CH>(F);
-#pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) {
+    // cross-lane stages over the LPG lanes of a group (DPP, in-row)
+    auto bstage = [&](auto mt) {
+      constexpr int m = decltype(mt)::value;
       const double sg = ((c & m) != 0) ? -1.0 : 1.0;
 #pragma unroll
-      for (int i = 0; i < CH; ++i) F[i] = __builtin_fma(F[i], sg, shfl_xor_f64(F[i], m));
-    }
+      for (int i = 0; i < CH; ++i) F[i] = __builtin_fma(F[i], sg, xor_lanes_f64<m>(F[i]));
+    };
+    if constexpr (LPG > 1) bstage(std::integral_constant<int, 1>{});
+    if constexpr (LPG > 2) bstage(std::integral_constant<int, 2>{});
+    if constexpr (LPG > 4) bstage(std::integral_constant<int, 4>{});
     // integers of the band quantum 2^q_b, q_b = E - (band+1)*kBand - 133
 #pragma unroll
     for (int i = 0; i < CH; ++i) {

@@ -690,19 +690,22 @@ struct TeamShape {
   int rpb;    // rows per block
 };
 
-// Choose a block of whole waves holding as many whole rows as fit, with the
-// least idle lanes (at most 512 threads, at most 256 rows).
-TeamShape team_shape(int T) {
+// Choose a block of whole waves holding whole rows of T lanes (at most 512
+// threads, at most 256 rows) for a persistent kernel with `wpc` resident
+// waves per CU: the most row lanes at work per CU (resident blocks x rows per
+// block x T), ties to the smaller block.
+TeamShape team_shape(int T, int wpc) {
   TeamShape best{T, 0, 0};
-  double best_waste = 2.0;
+  int best_lanes = 0;
   for (int waves = 1; waves <= 8; ++waves) {
     const int threads = 64 * waves;
     int rpb = threads / T;
     if (rpb < 1) continue;
     if (rpb > 256) rpb = 256;
-    const double waste = 1.0 - (double)(rpb * T) / threads;
-    if (waste < best_waste - 1e-9) {
-      best_waste = waste;
+    const int blocks = wpc / waves > 0 ? wpc / waves : 1;
+    const int lanes = blocks * rpb * T;
+    if (lanes > best_lanes) {
+      best_lanes = lanes;
       best.block = threads;
       best.rpb = rpb;
     }
@@ -720,9 +723,12 @@ constexpr int kFastWavesPerCU = CONVROT_FAST_WAVES_PER_CU;
 template <int G>
 hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
                        const SignMask& sm, bool f16, hipStream_t st) {
-  const TeamShape ts = team_shape(K / 64);
+  const TeamShape ts = team_shape(K / 64, kFastWavesPerCU);
   const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
-  const int64_t cap = (int64_t)kNumCUs * kFastWavesPerCU / (ts.block / 64);
+  // whole blocks per CU that stay resident together: a grid beyond that would
+  // run a second, partial round of blocks
+  const int per_cu = kFastWavesPerCU / (ts.block / 64);
+  const int64_t cap = (int64_t)kNumCUs * (per_cu > 0 ? per_cu : 1);
   const int64_t blocks = nbatches < cap ? nbatches : cap;
   auto kern = f16 ? rotate_quant_fast_kernel<G, true> : rotate_quant_fast_kernel<G, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ts.block), 0, st, x, xq, s, rows, K,
@@ -744,11 +750,11 @@ constexpr int kDeferredWavesPerCU = CONVROT_DEFERRED_WAVES_PER_CU;
 template <int G>
 hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,
                         int64_t rows, int K, const SignMask& sm, int mode, hipStream_t st) {
-  const TeamShape ts = team_shape(K / 32);
-  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
   const int wpc = mode == kRowDeferred ? kDeferredWavesPerCU : kExactWavesPerCU;
-  int64_t cap = (int64_t)kNumCUs * wpc / (ts.block / 64);
-  if (cap < 1) cap = 1;
+  const TeamShape ts = team_shape(K / 32, wpc);
+  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
+  const int per_cu = wpc / (ts.block / 64);  // whole resident blocks per CU
+  const int64_t cap = (int64_t)kNumCUs * (per_cu > 0 ? per_cu : 1);
   const int64_t blocks = nbatches < cap ? nbatches : cap;
   // rows the fast kernel left get a rounded float64 transform first
   auto kern = mode == kRowDeferred ? rotate_quant_exact_kernel<G, true>

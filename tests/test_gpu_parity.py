@@ -511,3 +511,48 @@ def test_ex_bf16_matches_named_entry_points():
     assert torch.equal(xq1, xq2) and torch.equal(sx1, sx2)
     assert torch.equal(cr.convrot_dequant_derotate_ex(wq, s_w, g, SEED),
                        cr.convrot_dequant_derotate(wq, s_w, g, SEED))
+
+
+# --------------------------------------------------------------------------
+# Seeded random shapes through the whole forward (every format and scale
+# granularity), against the oracle
+# --------------------------------------------------------------------------
+
+def _random_cases(count=12, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        g = int(rng.choice(GS))
+        k = int(rng.integers(1, 13)) * max(64, g)
+        n = int(rng.integers(1, 40)) * 16
+        m = int(rng.integers(1, 700))
+        cases.append((m, n, k, g, bool(rng.integers(0, 2)), str(rng.choice(["bf16", "f16"])),
+                      int(rng.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("m,n,k,g,pc,fmt,seed", _random_cases())
+def test_random_shapes_linear(m, n, k, g, pc, fmt, seed):
+    _announce(f"random linear m={m} n={n} k={k} g={g} pc={pc} {fmt}")
+    rng = np.random.default_rng(seed)
+    x32 = (rng.standard_normal((m, k)) * np.where(rng.random(k) < 0.01, 20.0, 1.0)).astype(np.float32)
+    w32 = (rng.standard_normal((n, k)) * 0.02 * 2.0 ** rng.integers(-6, 7, n)[:, None]).astype(np.float32)
+    b32 = rng.standard_normal(n).astype(np.float32)
+    enc = synth.f32_to_f16_bits if fmt == "f16" else synth.f32_to_bf16_bits
+    dtype = torch.float16 if fmt == "f16" else torch.bfloat16
+    xb, wb, bb = enc(x32), synth.f32_to_bf16_bits(w32), enc(b32)
+    wq_ref, s_ref = (oracle.quantize_weights_per_channel if pc else oracle.quantize_weights)(
+        wb, g, SEED)
+    y_ref = oracle.linear_int8(xb, wq_ref, s_ref, g, SEED, bb, fmt)[0]
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dtype).to(DEV)
+    q = cr.convrot_quantize_weights_per_channel if pc else cr.convrot_quantize_weights
+    wq, s_w = q(dev_bf16(wb), g, SEED)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert np.array_equal(f32_bits(s_w.cpu().numpy()), f32_bits(np.atleast_1d(s_ref)))
+    # a workspace of a random number of rows: random slicing as well
+    rows = int(rng.integers(1, m + 1))
+    ws = torch.empty(cr.convrot_linear_int8_workspace_for_rows(rows, k), dtype=torch.uint8,
+                     device=DEV)
+    y = cr.convrot_linear_int8_ex(to_dev(xb), wq, s_w, g, SEED, to_dev(bb), per_channel=pc,
+                                  workspace=ws)
+    assert np.array_equal(host_bits(y), y_ref)

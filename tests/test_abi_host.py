@@ -233,3 +233,20 @@ def test_session_argument_checks_without_gpu(lib):
     t, e, lt = ctypes.c_int(), ctypes.c_double(), ctypes.c_int()
     assert lib.convrot_session_lookup(None, 8, 64, 256, 256, 0, 0, ctypes.byref(t),
                                       ctypes.byref(e), ctypes.byref(lt)) == 1
+
+
+def test_header_compiles_and_links_as_c99(lib, tmp_path):
+    """include/convrot.h from plain C99 (gcc -std=c99 -pedantic), every entry
+    point referenced with its declared types, linked against the library"""
+    import shutil
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no gcc")
+    src = os.path.join(ROOT, "tests", "c", "header_c99.c")
+    obj = tmp_path / "header_c99.so"
+    r = subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Werror", "-fPIC", "-shared",
+                        "-I", os.path.join(ROOT, "include"), src, "-o", str(obj),
+                        cr.library_path(), "-Wl,--no-undefined",
+                        "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -226,6 +226,27 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     wait_vmcnt<0>();
   };
 
+  // The scaled output tile is staged in LDS (the ring is free after the
+  // K-loop) with rows of PITCH bytes; then every wave of the block stores
+  // whole tile rows with 16-byte stores, so each 128-byte output line is
+  // written once instead of in 16-byte pieces by 8 different instructions.
+  constexpr int PITCH = BN * 2 + 16;
+  static_assert(BM * PITCH <= 160 * 1024, "staged output tile");
+  auto store_tile = [&]() {
+    wait_lgkm0();  // this wave's staging writes are done
+    lds_barrier();
+    constexpr int CPR16 = BN * 2 / 16;  // 16-byte pieces per tile row
+#pragma unroll 4
+    for (int idx = tid; idx < BM * CPR16; idx += 64 * (NW + NP)) {
+      const int r = idx / CPR16;
+      const int cc = idx - r * CPR16;
+      const int m = m0 + r, n = n0 + 8 * cc;
+      if (m < M && n < N)  // N % 16 == 0: a piece is all inside or all outside
+        *reinterpret_cast<u4*>(y + (int64_t)m * N + n) =
+            *reinterpret_cast<const u4*>(lds + r * PITCH + 16 * cc);
+    }
+  };
+
   if constexpr (NP > 0) {
     if (wave >= NW) {
       // ---- producer: stage s+1 landed before the barrier that ends step
@@ -243,6 +264,10 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
         if (s + LA < nk) issue(s + LA, (s + LA) % NS);
       }
       lds_barrier();  // the consumers' last-step barrier
+      if (y) {
+        lds_barrier();  // the consumers' barrier before staging the tile
+        store_tile();
+      }
       return;
     }
   } else {
@@ -350,7 +375,12 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   }
 
   // ---- epilogue: 32x32 output layout: lane holds m = lane % 32 of the
-  // tile and n = 8*a + 4*(lane/32) + e for register 4a + e ----
+  // tile and n = 8*a + 4*(lane/32) + e for register 4a + e; the results go
+  // to the LDS staging tile, then out by store_tile ----
+  if (y) {
+    wait_lgkm0();  // every wave's last ring reads are done before the tile is staged
+    lds_barrier();
+  }
   const float sw = PC ? 0.0f : *s_w;
   // per-channel: the 4 consecutive columns of each (i, a) register group,
   // loaded once for all NJ row blocks
@@ -368,14 +398,16 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int m = m0 + wm * WTM + j * 32 + fr;
+    const int ml = wm * WTM + j * 32 + fr;  // row within the tile
+    const int m = m0 + ml;
     if (m >= M) continue;
     const float sx = s_x[m];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int n = n0 + wn * WTN + i * 32 + 8 * a + 4 * fh;
+        const int nl = wn * WTN + i * 32 + 8 * a + 4 * fh;  // column within the tile
+        const int n = n0 + nl;
         if (n >= N) continue;
         const v16i& v = acc[i][j];
         if (acc_out) {
@@ -397,11 +429,12 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
         }
         if (y) {
           const u2 o = {pack16x2<F16>(f[0], f[1]), pack16x2<F16>(f[2], f[3])};
-          *reinterpret_cast<u2*>(y + (int64_t)m * N + n) = o;
+          *reinterpret_cast<u2*>(lds + ml * PITCH + 2 * nl) = o;
         }
       }
     }
   }
+  if (y) store_tile();
 }
 
 struct TileCfg {
@@ -412,7 +445,10 @@ template <bool PC, bool F16, int BM, int BN, int BK, int WM, int WN, int NS, int
 hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                       const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
                       hipStream_t st) {
-  constexpr int lds_bytes = NS * (BM + BN) * BK;
+  // the K-loop's ring, or the staged output tile (rows of 2 BN + 16 bytes)
+  constexpr int ring_bytes = NS * (BM + BN) * BK;
+  constexpr int tile_bytes = BM * (BN * 2 + 16);
+  constexpr int lds_bytes = ring_bytes > tile_bytes ? ring_bytes : tile_bytes;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
   auto kern = gemm_i8_kernel<BM, BN, BK, WM, WN, NS, MINB, NP, PC, F16>;
   static bool attr = false;  // benign race: the call is idempotent

@@ -147,9 +147,9 @@ def _cpu_baseline(layer, g, seed, target_s):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the layer shards by tokens or output features without communication, see "
-              "DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the layer "
+              "shards by tokens or output features without any communication, so a "
+              "multi-GPU figure is the one-GPU figure per GPU", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -37,8 +37,10 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20
-SLEEP_CYCLES = 50_000_000  # GPU-side hold before a timed batch of launches
-WARM_LAUNCHES = 5  # untimed launches between the sleep and the first event
+HOLD_MS = 20.0        # minimum GPU-side hold before a launch-bound timed batch
+HOLD_CYCLES_PER_MS = 2.4e6  # torch.cuda._sleep counts shader clocks (~2.4 GHz)
+WARM_GPU_MS = 20.0    # untimed GPU work between the hold and the first event
+MIN_WARM, MAX_WARM = 2, 4000
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_zimage_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "int8_gemm_amd", "csrc", "gemm.hip")
 
@@ -55,6 +57,12 @@ def _parse():
                     help="target CPU time of the oracle sample (10-30 s)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the headline line: one JSON line per workload config "
+                         "(GEMM, linear, act-quant and dequant, HIP-event means)")
+    ap.add_argument("--warm-ms", type=float, default=WARM_GPU_MS,
+                    help="untimed GPU work before each timed batch (clock ramp); counter "
+                         "passes, which time nothing, may set it to 0")
     return ap.parse_args()
 
 
@@ -76,22 +84,58 @@ def _traffic(n_launch_units: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def _events_time(fn, reps, stream):
-    """GPU duration per launch from HIP events recorded on `stream`. The stream
-    is first held by a GPU sleep long enough for the host to enqueue every
-    call, so the events bracket the kernels alone, not host launch gaps; a
-    few untimed launches after the sleep bring the clocks back up before the
-    first event. Returns (mean, min, median) in ms: the mean over a batch of
-    `reps` back-to-back launches between two events (per-event overhead
-    amortised, as a kernel trace sees it; the median of 3 such batches), min
-    and median over launches bracketed one by one."""
+def _probe_ms(fn, stream):
+    """(GPU ms per launch, host ms per call) of `fn` from a short batch of
+    ~2 ms. The events measure the kernel itself when the host enqueues faster
+    than the GPU runs it, else (a launch-bound call) about the host's rate."""
     import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn(0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = int(min(100, max(1, 2.0 / max(e0.elapsed_time(e1), 1e-3))))
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    host = (time.perf_counter() - t0) * 1e3 / n
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, host
+
+
+def _events_time(fn, reps, stream):
+    """GPU duration per launch from HIP events recorded on `stream`.
+
+    Every timed batch follows WARM_GPU_MS of untimed launches of the same
+    call, so caches and clocks are in their steady state. A call whose kernel
+    runs less than twice as long as the host takes to issue it would leave
+    launch gaps: for those the stream is first held by a GPU-side sleep long
+    enough for the host to enqueue the warm-up and the batch (the host's
+    per-call cost is measured first); the clocks fall during the hold, and
+    the warm-up brings them back. Longer kernels need no hold: the host gets
+    ahead of the GPU on its own. Returns (mean, min, median) in ms: the mean
+    over a batch of `reps` back-to-back launches between two events
+    (per-event overhead amortised, as a kernel trace sees it; the median of 3
+    such batches), min and median over launches bracketed one by one."""
+    import torch
+    kern_ms, host_ms = _probe_ms(fn, stream)
+    warm = int(min(MAX_WARM, max(MIN_WARM, math.ceil(WARM_GPU_MS / max(kern_ms, 1e-4)))))
+
+    def held_warm(margin):
+        # margin: host cost per call relative to the probe's (event records add to it)
+        if kern_ms < 2.0 * margin * host_ms:
+            hold_ms = max(HOLD_MS, 1.5 * margin * (warm + reps) * host_ms)
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(int(hold_ms * HOLD_CYCLES_PER_MS))
+        for i in range(warm):
+            fn(i)
+
     means = []
     for _ in range(3):
-        with torch.cuda.stream(stream):
-            torch.cuda._sleep(SLEEP_CYCLES)
-        for i in range(WARM_LAUNCHES):
-            fn(i)
+        held_warm(1.0)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -103,8 +147,7 @@ def _events_time(fn, reps, stream):
     mean = sorted(means)[1]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(SLEEP_CYCLES)
+    held_warm(2.0)
     for i in range(reps):
         starts[i].record(stream)
         fn(i)
@@ -144,13 +187,88 @@ def _cpu_baseline(layer, g, seed, target_s):
                       f"{el:.1f} s"}
 
 
+def _all_configs(reps: int):
+    """One JSON line per workload config: the GEMM (default tile), the whole
+    int8 forward with the default workspace, the activation quantization and
+    the dequant + derotate, each as the HIP-event mean of back-to-back
+    launches; input and output buffers rotated so that the data touched
+    between two uses of a buffer exceeds twice the 256 MB MALL (footprints of
+    at least 512 MB need no rotation)."""
+    import numpy as np
+    import torch
+
+    import int8_gemm_amd as cr
+    import synth
+
+    cr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    seed = synth.ROT_SEED
+    cases = [(synth.TINY, 256), (synth.ZIMAGE_ATTN, 256), (synth.FLUX_MLP_UP, 256),
+             (synth.FLUX_MLP_DOWN, 256), (synth.WAN_FFN_UP, 256), (synth.WAN_FFN_DOWN, 256)] + \
+        [(synth.QKV_SWEEP, g) for g in synth.GROUP_SIZES]
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def copies(t, footprint):
+        n = 1 if footprint >= 2 * MALL_BYTES else max(2, math.ceil(2 * MALL_BYTES / footprint) + 1)
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    for layer, g in cases:
+        print(f"[bench] config {layer.name} g={g}", file=sys.stderr, flush=True)
+        m, n, k = layer.m, layer.n, layer.k
+        x0 = to_dev(layer.x())
+        wq, s_w = cr.convrot_quantize_weights(to_dev(layer.w()), g, seed)
+        xs = copies(x0, 3 * m * k)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sx = torch.empty(m, dtype=torch.float32, device=dev)
+        cr.convrot_quantize_activations(x0, g, seed, xq=xq, s_x=sx)
+        ys = copies(torch.empty((m, n), dtype=torch.bfloat16, device=dev), 2 * m * n)
+        ws = torch.empty(cr.convrot_linear_int8_workspace_size(m, n, k), dtype=torch.uint8,
+                         device=dev)
+        act_ms, _, _ = _events_time(lambda i: cr.convrot_quantize_activations(
+            xs[i % len(xs)], g, seed, xq=xq, s_x=sx), reps, stream)
+        gemm_ms, _, _ = _events_time(lambda i: cr.convrot_gemm_int8(
+            xq, sx, wq, s_w, y=ys[i % len(ys)]), reps, stream)
+        lin_ms, _, _ = _events_time(lambda i: cr.convrot_linear_int8(
+            xs[i % len(xs)], wq, s_w, g, seed, workspace=ws, out=ys[i % len(ys)]), reps, stream)
+        del xs, ys, ws, xq
+        wqs = copies(wq, 3 * n * k)
+        outs = copies(torch.empty((n, k), dtype=torch.bfloat16, device=dev), 3 * n * k)
+        deq_ms, _, _ = _events_time(lambda i: cr.convrot_dequant_derotate(
+            wqs[i % len(wqs)], s_w, g, seed, out=outs[i % len(outs)]), reps, stream)
+        del wqs, outs
+        torch.cuda.synchronize()
+        ops = 2.0 * m * n * k
+        act_b, deq_b = 3.0 * m * k + 4.0 * m, 3.0 * n * k + 4.0
+        print(json.dumps({
+            "config": layer.name, "m": m, "n": n, "k": k, "g": g,
+            "gemm_TOPS": round(ops / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_peak": round(ops / (gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "linear_TOPS": round(ops / (lin_ms * 1e-3) / 1e12, 1),
+            "act_quant_GB/s": round(act_b / (act_ms * 1e-3) / 1e9, 1),
+            "act_quant_frac_hbm": round(act_b / (act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "dequant_GB/s": round(deq_b / (deq_ms * 1e-3) / 1e9, 1),
+            "dequant_frac_hbm": round(deq_b / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "us": {"gemm": round(gemm_ms * 1e3, 2), "linear": round(lin_ms * 1e3, 2),
+                   "act_quant": round(act_ms * 1e3, 2), "dequant": round(deq_ms * 1e3, 2)}}),
+            flush=True)
+
+
 def main():
+    global WARM_GPU_MS
     args = _parse()
+    WARM_GPU_MS = max(0.0, args.warm_ms)
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the layer "
               "shards by tokens or output features without any communication, so a "
               "multi-GPU figure is the one-GPU figure per GPU", file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        _all_configs(min(max(args.steps, 10), 50))
+        return
 
     import numpy as np
     import torch

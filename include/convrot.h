@@ -164,8 +164,10 @@ convrot_status convrot_gemm_int8(const int8_t* xq, const float* s_x, const int8_
                                  const float* s_w, const uint16_t* bias, int64_t m, int64_t n,
                                  int64_t k, uint16_t* y, int32_t* acc, void* stream);
 
-/* Test / tuning hook: convrot_gemm_int8 with a forced block tile of tile x tile
- * outputs (128, 192 or 256; 0 = the automatic choice). Same results. */
+/* Test / tuning hook: convrot_gemm_int8 with a forced block tile: 128, 192 or
+ * 256 (tile x tile outputs), 384 (384 x 192 outputs; only for k % 128 == 0),
+ * or 0 = the automatic choice. Same results. Any other tile value, or 384 with
+ * k % 128 != 0, is CONVROT_E_INVALID_ARG before anything is launched. */
 convrot_status convrot_gemm_int8_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
                                       const float* s_w, const uint16_t* bias, int64_t m,
                                       int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
@@ -213,7 +215,7 @@ convrot_status convrot_linear_int8_per_channel(const uint16_t* x, const int8_t* 
  *   convrot_quantize_activations_ex: x [m, k] -> xq [m, k] int8, s_x [m]
  *   convrot_dequant_derotate_ex:     wq [n, k], s_w -> w_out [n, k] in out_dtype
  *   convrot_gemm_int8_ex:            y (nullable) in dtype, acc (nullable);
- *                                    tile 0 = automatic, else 128/192/256
+ *                                    tile as for convrot_gemm_int8_tile
  *   convrot_linear_int8_ex:          x, bias, y in dtype; same workspace rules */
 convrot_status convrot_quantize_activations_ex(const void* x, convrot_dtype dtype, int64_t m,
                                                int64_t k, int g, uint64_t rot_seed, int8_t* xq,

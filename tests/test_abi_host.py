@@ -81,6 +81,25 @@ def test_rotating_entry_points_reject_bad_group_and_shape(lib, g, k, want):
     assert lib.convrot_last_error_string()
 
 
+@pytest.mark.parametrize("tile,k,why", [(100, 256, "not supported"), (-1, 256, "not supported"),
+                                        (512, 256, "not supported"), (384, 320, "k % 128"),
+                                        (384, 192, "k % 128"), (384, 256, "null pointer"),
+                                        (128, 320, "null pointer"), (0, 320, "null pointer")])
+def test_forced_tile_is_checked_before_launch(lib, tile, k, why):
+    """Unsupported tiles, and the 384 x 192 tile without 128-byte K-steps, are
+    refused before any HIP call; accepted tiles get as far as the null-output
+    check (m = 8, y = acc = null), which also refuses before any launch."""
+    calls = [("convrot_gemm_int8_tile", (FAKE, FAKE, FAKE, FAKE, None, 8, 16, k, None, None,
+                                         tile, None)),
+             ("convrot_gemm_int8_per_channel_tile", (FAKE, FAKE, FAKE, FAKE, None, 8, 16, k, None,
+                                                     None, tile, None))]
+    calls += [("convrot_gemm_int8_ex", (FAKE, FAKE, FAKE, FAKE, 0, None, 8, 16, k, None, None, dt,
+                                        tile, None)) for dt in (0, 1)]
+    for fn, args in calls:
+        assert _status(lib, fn, *args) == 1, fn
+        assert why in lib.convrot_last_error_string().decode(), fn
+
+
 def test_null_and_misaligned_and_overlap(lib):
     assert _status(lib, "convrot_quantize_activations", None, 8, 256, 256, 1, FAKE, FAKE,
                    None) == 1

@@ -335,8 +335,6 @@ def test_per_channel_square_weight_decodes_rows_not_columns(g):
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (255, 16, 192), (257, 272, 320), (33, 1040, 64),
                                    (400, 592, 384), (300, 400, 1152), (800, 208, 256)])
 def test_per_channel_gemm_shapes(m, n, k, tile):
-    if tile == 384 and k % 128:
-        pytest.skip("the 384 x 192 tile needs K % 128 == 0")
     _announce(f"per-channel gemm shape {m}x{n}x{k} tile={tile}")
     rng = np.random.default_rng(m * 5 + n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
@@ -344,6 +342,13 @@ def test_per_channel_gemm_shapes(m, n, k, tile):
     sx = (rng.random(m) * 1e-3).astype(np.float32)
     sw = (rng.random(n) * 2.0 ** rng.integers(-20, 0, n)).astype(np.float32)
     bias = synth.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    if tile == 384 and k % 128:
+        # the 384 x 192 tile exists only for 128-byte K-steps: refused, nothing launched
+        with pytest.raises(cr.ConvrotError, match="k % 128"):
+            cr.convrot_gemm_int8_per_channel(
+                torch.from_numpy(xq).to(DEV), _dev_f32(sx), torch.from_numpy(wq).to(DEV),
+                _dev_f32(sw), None, want_acc=True, tile=tile)
+        return
     for b in (None, bias):
         y, acc = cr.convrot_gemm_int8_per_channel(
             torch.from_numpy(xq).to(DEV), _dev_f32(sx), torch.from_numpy(wq).to(DEV),
@@ -447,8 +452,6 @@ def test_f16_edge_rows(g):
 @pytest.mark.parametrize("tile", [0, 128, 192, 256, 384])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (257, 272, 320), (300, 400, 1152)])
 def test_f16_gemm_shapes(m, n, k, tile, per_channel):
-    if tile == 384 and k % 128:
-        pytest.skip("the 384 x 192 tile needs K % 128 == 0")
     _announce(f"f16 gemm {m}x{n}x{k} tile={tile} pc={per_channel}")
     rng = np.random.default_rng(m + 3 * n)
     xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
@@ -457,6 +460,15 @@ def test_f16_gemm_shapes(m, n, k, tile, per_channel):
     sx[0] = np.float32(50.0)          # row 0 overflows half in places: inf
     sw = (rng.random(n) * 1e-2).astype(np.float32) if per_channel else np.float32(4e-3)
     bias = synth.f32_to_f16_bits(rng.standard_normal(n).astype(np.float32))
+    if tile == 384 and k % 128:
+        # the 384 x 192 tile exists only for 128-byte K-steps: refused, nothing launched
+        with pytest.raises(cr.ConvrotError, match="k % 128"):
+            cr.convrot_gemm_int8_ex(
+                torch.from_numpy(xq).to(DEV), torch.from_numpy(sx).to(DEV),
+                torch.from_numpy(wq).to(DEV),
+                torch.from_numpy(np.atleast_1d(sw).astype(np.float32)).to(DEV), None,
+                per_channel=per_channel, dtype=torch.float16, want_acc=True, tile=tile)
+        return
     for b in (None, bias):
         y, acc = cr.convrot_gemm_int8_ex(
             torch.from_numpy(xq).to(DEV), torch.from_numpy(sx).to(DEV),

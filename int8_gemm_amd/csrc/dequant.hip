@@ -230,10 +230,10 @@ hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channe
   const int64_t tiles = (nrows + 31) / 32;
   const int tpb = (R / 32 >= 4) ? 1 : 4;  // tiles per block step
   const int64_t chunks = (tiles + tpb - 1) / tpb;
-#ifndef CONVROT_DEQUANT_BLOCKS_PER_CU
-#define CONVROT_DEQUANT_BLOCKS_PER_CU 4
-#endif
-  const int64_t cap = (int64_t)kNumCUs * CONVROT_DEQUANT_BLOCKS_PER_CU;  // persistent blocks
+  // persistent blocks per CU, as measured: 2 when a block step is one tile
+  // (g = 256; 4 blocks were 4-18% slower on 3072x3072 .. 13824x5120), 4 when
+  // it is four (g <= 64, where 2 or 3 were up to 11% slower)
+  const int64_t cap = (int64_t)kNumCUs * (tpb == 1 ? 2 : 4);
   const int64_t blocks = chunks < cap ? chunks : cap;
   const int vrows_per_ch = (int)(k / R);  // K % R == 0 for every supported (K, g)
   const bool pc = sw_per_channel, f16 = dt == DType::kF16;

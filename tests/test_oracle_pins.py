@@ -17,6 +17,8 @@ import torch
 
 import oracle as o
 import synth
+from exact_rounding import (EPILOGUE_ORDER_CASES, QUANT_ORDER_CASES, epilogue_scales_first,
+                            epilogue_weight_first, f32, quant_divide, quant_reciprocal, rn32)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SEED = synth.ROT_SEED
@@ -293,6 +295,59 @@ def test_epilogue_closed_form():
     assert np.array_equal(y, o.f32_to_bf16(t.astype(np.float32)))
     # 2^24 + 1 is not a float32: it rounds to 2^24 before scaling
     assert acc.astype(np.float32)[0, 3] == np.float32(2 ** 24)
+
+
+# --------------------------------------------------------------------------
+# P4b, P5b: operation order of the quantizer and of the epilogue, pinned with
+# exact rational arithmetic (fractions.Fraction) written here, not with the
+# oracle's own expressions. Each case is an input where the two plausible
+# readings of the same formula give different results, so a swapped order
+# fails. The inputs were found by a search for such disagreements; every
+# expected value below is derived in this file.
+# --------------------------------------------------------------------------
+
+def test_quantize_op_order_reciprocal_not_divide():
+    """The int8 code is rint(RN32(v * RN32(127/amax))), not rint(RN32(v /
+    RN32(amax/127))): the multiply-by-reciprocal reading of the quantizer's
+    round(clip(Wr / s_w)) (convert_to_quant guide, "How INT8 ConvRot
+    Quantization Works"; the scale itself stays s = RN32(amax/127))."""
+    for vs, ams in QUANT_ORDER_CASES:
+        v, amax = Fraction(float.fromhex(vs)), Fraction(float.fromhex(ams))
+        want, other = quant_reciprocal(v, amax), quant_divide(v, amax)
+        assert want != other, (vs, ams)
+        q, s = o.quantize_with_amax(np.array([[f32(v), f32(amax)]], dtype=np.float32),
+                                    np.array([f32(amax)], dtype=np.float32))
+        assert int(q[0, 0]) == want, (vs, ams, int(q[0, 0]), want, other)
+        assert int(q[0, 1]) == 127
+        assert Fraction(float(s[0])) == rn32(amax / 127)
+
+
+def test_epilogue_op_order_weight_scale_first():
+    """y = RN_bf16(RN32(RN32(acc * s_w) * s_x[m])): the accumulator is scaled
+    by the weight scale, then by the token's scale (Invoke docs "int8
+    Compute", introduction: the int8 product is rescaled to the compute
+    dtype; the pages give no order, this is the reading taken)."""
+    for acc, sws, sxs in EPILOGUE_ORDER_CASES:
+        sw, sx = Fraction(float.fromhex(sws)), Fraction(float.fromhex(sxs))
+        want, other = epilogue_weight_first(acc, sw, sx), epilogue_scales_first(acc, sw, sx)
+        assert want != other, (acc, sws, sxs)
+        y = o.epilogue(np.array([[acc]], dtype=np.int32), f32(sw),
+                       np.array([f32(sx)], dtype=np.float32))
+        got = Fraction(float(o.bf16_to_f64(y)[0, 0]))
+        assert got == want, (acc, sws, sxs, float(got), float(want), float(other))
+
+
+def test_rounding_helpers_against_numpy():
+    """The rational rounding above agrees with numpy's IEEE single rounding on
+    random quotients (so the pins above test the oracle, not the helpers)."""
+    rng = np.random.default_rng(21)
+    a = rng.standard_normal(300).astype(np.float32)
+    b = (rng.standard_normal(300) * 2.0 ** rng.integers(-40, 40, 300)).astype(np.float32)
+    for x, y in zip(a, b):
+        if y == 0:
+            continue
+        assert rn32(Fraction(float(x)) / Fraction(float(y))) == Fraction(float(np.float32(x / y)))
+        assert rn32(Fraction(float(x)) * Fraction(float(y))) == Fraction(float(np.float32(x * y)))
 
 
 # --------------------------------------------------------------------------

@@ -127,10 +127,15 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def f32_to_bf16(a: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bits, round to nearest, ties to even (finite inputs)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    """float32 -> bf16 bits, round to nearest, ties to even (finite inputs):
+    add 0x7FFF plus the kept lowest bit, drop the low 16 bits. For finite
+    values the sum stays below 2^32, so uint32 arithmetic is exact."""
+    u = np.array(a, dtype=np.float32).view(np.uint32)  # a private copy
     lsb = (u >> 16) & 1
-    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u += lsb
+    u += 0x7FFF
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def f16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -345,12 +350,14 @@ def _row_scales(s_w, n: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def derotation_integers(wq: np.ndarray, g: int, seed: int) -> np.ndarray:
-    """S = (Wq . D) . H per g-group of the input axis, exact int64 [N, K]."""
+    """S = (Wq . D) . H per g-group of the input axis, exact int64 [N, K].
+    The product runs in float64 BLAS: every partial sum is an integer of
+    magnitude <= 127 * g < 2^53, so it is exact."""
     n, kdim = wq.shape
     d = rotation_signs(seed, g)
     h = hadamard(g)
-    grp = wq.reshape(-1, g).astype(np.int64) * d[None, :]
-    return (grp @ h).reshape(n, kdim)
+    grp = wq.reshape(-1, g).astype(np.float64) * d[None, :].astype(np.float64)
+    return (grp @ h.astype(np.float64)).astype(np.int64).reshape(n, kdim)
 
 
 def dequant_derotate(wq: np.ndarray, s_w, g: int, seed: int, out_dtype: str = "bf16") -> np.ndarray:

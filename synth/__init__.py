@@ -35,9 +35,11 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
     Input preparation only. Inputs here are finite.
     """
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    u = u.astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.array(a, dtype=np.float32).view(np.uint32)  # a private copy
+    lsb = (u >> 16) & 1
+    u += lsb       # finite values stay below 2^32 (at most 0xFF7FFFFF + 0x8000)
+    u += 0x7FFF
+    u >>= 16
     return u.astype(np.uint16)
 
 

@@ -363,6 +363,12 @@ def test_dequant_integers_independent(g):
     dense = np.kron(np.eye(512 // g, dtype=np.int64), dh)     # blockdiag(D H)
     assert np.array_equal(o.derotation_integers(wq, g, SEED), wq.astype(np.int64) @ dense)
     assert np.abs(o.derotation_integers(wq, g, SEED)).max() <= 127 * g
+    # the extreme: a row of 127 d reaches S = 127 g (and -127 d gives -127 g)
+    wq[0, :g] = 127 * d
+    wq[1, :g] = -127 * d
+    s_int = o.derotation_integers(wq, g, SEED)
+    assert s_int[0, 0] == 127 * g and s_int[1, 0] == -127 * g
+    assert np.array_equal(s_int, wq.astype(np.int64) @ dense)
 
 
 @pytest.mark.parametrize("g", GS)

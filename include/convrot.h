@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 5
+#define CONVROT_ABI_VERSION 6
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -319,6 +319,43 @@ size_t convrot_linear_int8_workspace_size(int64_t m, int64_t n, int64_t k);
 /* Host-only: the rotation signs d[0..g) for (g, rot_seed) as +1/-1 bytes into
  * host memory `d` (g bytes). Touches no GPU. */
 convrot_status convrot_rotation_signs(uint64_t rot_seed, int g, int8_t* d);
+
+/* Machine shape. Persistent grids, the GEMM's tile choice and its XCD-aware
+ * tile order are sized from the device's compute-unit count, queried once
+ * per device (hipDeviceAttributeMultiprocessorCount: 256 on an MI355X, fewer
+ * on a compute partition); the XCD count is CUs / 32, the CUs of one gfx950
+ * XCD (1 below 64 CUs). Sizing changes speed only, never results.
+ *
+ * convrot_compute_units: the count that launches on the current device use.
+ * convrot_set_compute_units: a process-wide override of that count for
+ *   tests and tuning (0 restores the device's count); e.g. a small count
+ *   makes every persistent grid walk many passes. It affects launches
+ *   enqueued after the call, from any thread.
+ * convrot_plan_launch: host only (touches no GPU when compute_units > 0):
+ *   the launch geometry of `kernel` for the given shape (m rows for the
+ *   activation kernels, n x k for the dequant, m x n x k for the GEMM; g for
+ *   the rotating kernels) on `compute_units` CUs (0 = the current device's).
+ *   Shape errors as for the corresponding entry point. */
+typedef enum convrot_kernel {
+  CONVROT_KERNEL_ACT_QUANT = 0,          /* activation rotate + quantize, fast kernel   */
+  CONVROT_KERNEL_ACT_QUANT_DEFERRED = 1, /* its pass over the rows it defers            */
+  CONVROT_KERNEL_EXACT = 2,              /* exact kernel (weights, the _exact hook)     */
+  CONVROT_KERNEL_DEQUANT = 3,            /* dequant + derotate                          */
+  CONVROT_KERNEL_GEMM = 4                /* int8 GEMM, automatic tile                   */
+} convrot_kernel;
+typedef struct convrot_launch_plan {
+  int64_t grid;           /* workgroups                                                  */
+  int64_t passes;         /* persistent kernels: batches per workgroup (rounded up)      */
+  int32_t block;          /* threads per workgroup                                       */
+  int32_t rows_per_block; /* act-quant: token rows per batch; dequant: 32-row tiles/step */
+  int32_t tile_m, tile_n; /* GEMM block tile (0 otherwise)                               */
+  int32_t xcds;           /* XCDs of the GEMM's tile order                                */
+  int32_t compute_units;  /* the CU count the plan was made for                          */
+} convrot_launch_plan;
+int convrot_compute_units(void);
+convrot_status convrot_set_compute_units(int compute_units_override);
+convrot_status convrot_plan_launch(convrot_kernel kernel, int64_t m, int64_t n, int64_t k, int g,
+                                   int compute_units, convrot_launch_plan* out);
 
 const char* convrot_status_string(convrot_status s);
 /* Details of the last error on the calling thread ("" if none). */

@@ -27,7 +27,8 @@ __all__ = [
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
     "convrot_streamer_linear_int8", "Streamer", "convrot_session_create",
     "convrot_session_destroy", "convrot_session_linear_int8", "convrot_session_lookup",
-    "Session", "EXPORTED_SYMBOLS",
+    "Session", "EXPORTED_SYMBOLS", "convrot_compute_units", "convrot_set_compute_units",
+    "convrot_plan_launch", "KERNELS",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -49,8 +50,19 @@ EXPORTED_SYMBOLS = (
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
     "convrot_streamer_linear_int8", "convrot_session_create", "convrot_session_destroy",
-    "convrot_session_linear_int8", "convrot_session_lookup",
+    "convrot_session_linear_int8", "convrot_session_lookup", "convrot_compute_units",
+    "convrot_set_compute_units", "convrot_plan_launch",
 )
+
+# convrot_kernel values (convrot_plan_launch)
+KERNELS = {"act_quant": 0, "act_quant_deferred": 1, "exact": 2, "dequant": 3, "gemm": 4}
+
+
+class _LaunchPlan(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int64), ("passes", ctypes.c_int64), ("block", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("xcds", ctypes.c_int32),
+                ("compute_units", ctypes.c_int32)]
 
 # convrot_dtype and convrot_scale_mode values
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
@@ -115,6 +127,8 @@ def load_library():
                                             P],
             "convrot_session_lookup": [P, I64, I64, I64, I, I, I, ctypes.POINTER(I),
                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)],
+            "convrot_set_compute_units": [I],
+            "convrot_plan_launch": [I, I64, I64, I64, I, I, ctypes.POINTER(_LaunchPlan)],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -130,6 +144,8 @@ def load_library():
         lib.convrot_last_error_string.restype = ctypes.c_char_p
         lib.convrot_abi_version.argtypes = []
         lib.convrot_abi_version.restype = I
+        lib.convrot_compute_units.argtypes = []
+        lib.convrot_compute_units.restype = I
         _lib = lib
         return lib
 
@@ -173,6 +189,28 @@ def convrot_abi_version() -> int:
 
 def convrot_status_string(status: int) -> str:
     return load_library().convrot_status_string(status).decode()
+
+
+def convrot_compute_units() -> int:
+    """CUs that launches on the current device size their grids for."""
+    return int(load_library().convrot_compute_units())
+
+
+def convrot_set_compute_units(compute_units: int) -> None:
+    """Process-wide override of that count (tests and tuning); 0 restores the
+    device's count."""
+    _check(load_library().convrot_set_compute_units(compute_units))
+
+
+def convrot_plan_launch(kernel: str, m: int = 0, n: int = 0, k: int = 0, g: int = 256,
+                        compute_units: int = 0) -> dict:
+    """Launch geometry of `kernel` (a KERNELS key) for a shape on
+    `compute_units` CUs (0 = the current device's). Host only when
+    compute_units > 0."""
+    plan = _LaunchPlan()
+    _check(load_library().convrot_plan_launch(KERNELS[kernel], m, n, k, g, compute_units,
+                                              ctypes.byref(plan)))
+    return {f: int(getattr(plan, f)) for f, _ in _LaunchPlan._fields_}
 
 
 def convrot_rotation_signs(rot_seed: int, g: int) -> list[int]:

@@ -124,11 +124,85 @@ bool scale_mode_of(int v, bool* pc) {
 size_t sw_bytes(bool pc, int64_t n) { return pc ? (size_t)n * 4 : 4; }
 bool sw_aligned(bool pc, const float* s_w) { return aligned(s_w, pc ? 16 : 4); }
 
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];  // 0 = not queried yet
+std::atomic<int> g_cu_override{0};
+
 }  // namespace
+
+namespace convrot {
+
+int compute_units() {
+  const int forced = g_cu_override.load(std::memory_order_relaxed);
+  if (forced > 0) return forced;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return 256;
+    g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+}  // namespace convrot
 
 extern "C" {
 
 int convrot_abi_version(void) { return CONVROT_ABI_VERSION; }
+
+convrot_status convrot_set_compute_units(int compute_units_override) {
+  if (compute_units_override < 0 || compute_units_override > 1 << 16)
+    return fail(CONVROT_E_INVALID_ARG, "convrot_set_compute_units: %d", compute_units_override);
+  g_cu_override.store(compute_units_override, std::memory_order_relaxed);
+  return ok();
+}
+
+int convrot_compute_units(void) { return convrot::compute_units(); }
+
+convrot_status convrot_plan_launch(convrot_kernel kernel, int64_t m, int64_t n, int64_t k, int g,
+                                   int compute_units, convrot_launch_plan* out) {
+  const char* fn = "convrot_plan_launch";
+  if (!out) return fail(CONVROT_E_INVALID_ARG, "%s: null output", fn);
+  memset(out, 0, sizeof *out);
+  if (compute_units < 0) return fail(CONVROT_E_INVALID_ARG, "%s: compute_units < 0", fn);
+  const int cus = compute_units > 0 ? compute_units : convrot::compute_units();
+  LaunchPlan p;
+  switch (kernel) {
+    case CONVROT_KERNEL_ACT_QUANT:
+    case CONVROT_KERNEL_ACT_QUANT_DEFERRED:
+    case CONVROT_KERNEL_EXACT:
+      if (convrot_status s = check_rot(fn, m, k, g)) return s;
+      if (m == 0) return ok();
+      p = kernel == CONVROT_KERNEL_EXACT
+              ? plan_exact(m, (int)k, cus)
+              : plan_act_quant(m, (int)k, kernel == CONVROT_KERNEL_ACT_QUANT_DEFERRED, cus);
+      break;
+    case CONVROT_KERNEL_DEQUANT:
+      if (n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
+      if (convrot_status s = check_rot(fn, n, k, g)) return s;
+      p = plan_dequant(n, k, g, cus);
+      break;
+    case CONVROT_KERNEL_GEMM:
+      if (convrot_status s = check_gemm(fn, m, n, k)) return s;
+      if (m == 0) return ok();
+      p = plan_gemm(m, n, k, 0, cus);
+      break;
+    default:
+      return fail(CONVROT_E_INVALID_ARG, "%s: kernel=%d", fn, (int)kernel);
+  }
+  out->grid = p.grid;
+  out->block = p.block;
+  out->rows_per_block = p.rows_per_block;
+  out->tile_m = p.tile_m;
+  out->tile_n = p.tile_n;
+  out->xcds = p.xcds;
+  out->passes = p.passes;
+  out->compute_units = cus;
+  return ok();
+}
 
 const char* convrot_status_string(convrot_status s) {
   switch (s) {

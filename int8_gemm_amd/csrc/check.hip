@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void flush_kernel(u4* __restrict__ buf, int64_
 hipError_t launch_flush(void* buf, size_t bytes, hipStream_t st) {
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 == 0) return hipSuccess;
-  hipLaunchKernelGGL(flush_kernel, dim3(kNumCUs * 8), dim3(256), 0, st, static_cast<u4*>(buf),
+  hipLaunchKernelGGL(flush_kernel, dim3(compute_units() * 8), dim3(256), 0, st, static_cast<u4*>(buf),
                      n16);
   return hipGetLastError();
 }

@@ -24,8 +24,13 @@ __host__ __device__ constexpr int ilog2(int g) { return g <= 1 ? 0 : 1 + ilog2(g
 // (banded) kernel must finish. It is never a valid scale.
 constexpr uint32_t kDeferredRow = 0x7FC0DEADu;
 
-// Compute units of an MI355X (gfx950); sizes persistent grids.
-constexpr int kNumCUs = 256;
+// Compute units per XCD on gfx950 (an MI355X has 8 XCDs of 32 CUs; a
+// compute partition exposes whole XCDs). Workgroups of a launch are dealt to
+// the XCDs round-robin.
+constexpr int kCUsPerXCD = 32;
+__host__ __device__ constexpr int xcd_count(int cus) {
+  return cus >= 2 * kCUsPerXCD ? cus / kCUsPerXCD : 1;
+}
 
 // Bands of the exact rotation: each band spans at most kBand binades, so a
 // float64 Walsh-Hadamard transform over one band is exact (see rotate.hip).

@@ -220,28 +220,37 @@ static void launch_g(bool pc, bool f16, int64_t blocks, const int8_t* wq, const 
                      vrows_per_ch, 1.0 / (double)vrows_per_ch, sm, w_out);
 }
 
+// Persistent blocks per CU, as measured: 2 when a block step is one tile
+// (g = 256; 4 blocks were 4-18% slower on 3072x3072 .. 13824x5120), 4 when
+// it is four (g <= 64, where 2 or 3 were up to 11% slower).
+LaunchPlan plan_dequant(int64_t n, int64_t k, int g, int cus) {
+  LaunchPlan p;
+  p.block = 256;
+  const int R = g > 32 ? g : 32;
+  const int64_t nrows = n * k / R;
+  const int64_t tiles = (nrows + 31) / 32;
+  p.rows_per_block = (R / 32 >= 4) ? 1 : 4;  // 32-row tiles per block step
+  const int64_t chunks = (tiles + p.rows_per_block - 1) / p.rows_per_block;
+  const int64_t cap = (int64_t)(cus > 0 ? cus : 1) * (p.rows_per_block == 1 ? 2 : 4);
+  p.grid = chunks < cap ? chunks : cap;
+  p.passes = p.grid > 0 ? (chunks + p.grid - 1) / p.grid : 0;
+  return p;
+}
+
 hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,
                           int64_t k, int g, const SignMask& sm, uint16_t* w_out, DType dt,
                           hipStream_t st) {
-  const int64_t ne = n * k;
-  if (ne == 0) return hipSuccess;
+  if (n * k == 0) return hipSuccess;
+  const LaunchPlan p = plan_dequant(n, k, g, compute_units());
   const int R = g > 32 ? g : 32;
-  const int64_t nrows = ne / R;
-  const int64_t tiles = (nrows + 31) / 32;
-  const int tpb = (R / 32 >= 4) ? 1 : 4;  // tiles per block step
-  const int64_t chunks = (tiles + tpb - 1) / tpb;
-  // persistent blocks per CU, as measured: 2 when a block step is one tile
-  // (g = 256; 4 blocks were 4-18% slower on 3072x3072 .. 13824x5120), 4 when
-  // it is four (g <= 64, where 2 or 3 were up to 11% slower)
-  const int64_t cap = (int64_t)kNumCUs * (tpb == 1 ? 2 : 4);
-  const int64_t blocks = chunks < cap ? chunks : cap;
+  const int64_t nrows = n * k / R;
   const int vrows_per_ch = (int)(k / R);  // K % R == 0 for every supported (K, g)
   const bool pc = sw_per_channel, f16 = dt == DType::kF16;
   switch (g) {
-    case 4: launch_g<4>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 16: launch_g<16>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 64: launch_g<64>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    default: launch_g<256>(pc, f16, blocks, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 4: launch_g<4>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 16: launch_g<16>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    case 64: launch_g<64>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
+    default: launch_g<256>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
   }
   return hipGetLastError();
 }

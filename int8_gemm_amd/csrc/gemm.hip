@@ -26,8 +26,9 @@
 //     instruction fills 1024 / BK rows; within a row the 16-byte chunks are
 //     XOR-swizzled by row (below), which makes the fragment reads free of
 //     bank conflicts;
-//   * the block index is remapped so that each of the 8 XCDs gets a
-//     contiguous range of tiles, walked in groups of 8 tile rows (L2 reuse).
+//   * the block index is remapped so that each XCD (8 on an MI355X; the
+//     count follows the device's compute units) gets a contiguous range of
+//     tiles, walked in groups of 8 tile rows (L2 reuse).
 // Measured on MI355X (rocprofv3 counters): the K-loop is bound by the rate
 // at which each CU's vector L1 streams operands from L2 into LDS. A CU keeps
 // only some 40-70 L1->L2 requests in flight at ~300 cycles each, so per-CU
@@ -89,7 +90,7 @@ template <int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP, bool
 __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ s_x, const int8_t* __restrict__ wq,
     const float* __restrict__ s_w, const uint16_t* __restrict__ bias, int M, int N, int K,
-    int tiles_m, int tiles_n, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+    int tiles_m, int tiles_n, int nx, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
   constexpr int NW = WM * WN;                   // waves: WM along m, WN along n
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile (m, n)
   constexpr int NJ = WTM / 32, NI = WTN / 32;   // 32x32 MFMA tiles per wave (m, n)
@@ -125,11 +126,11 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   const int wm = wave / WN;
   const int cw = NP > 0 ? wave - NW : wave;  // index among the copying waves
 
-  // ---- tile index: XCD-contiguous ranges, grouped rows ----
+  // ---- tile index: XCD-contiguous ranges (workgroups are dealt to the nx
+  // XCDs round-robin), grouped rows ----
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   {
-    constexpr int nx = 8;
     const int per = (ntiles + nx - 1) / nx;
     const int xcd = bid % nx;
     const int loc = bid / nx;
@@ -444,7 +445,7 @@ struct TileCfg {
 template <bool PC, bool F16, int BM, int BN, int BK, int WM, int WN, int NS, int MINB, int NP = 0>
 hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, const float* s_w,
                       const uint16_t* bias, int m, int n, int k, uint16_t* y, int32_t* acc,
-                      hipStream_t st) {
+                      int nx, hipStream_t st) {
   // the K-loop's ring, or the staged output tile (rows of 2 BN + 16 bytes)
   constexpr int ring_bytes = NS * (BM + BN) * BK;
   constexpr int tile_bytes = BM * (BN * 2 + 16);
@@ -460,8 +461,8 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
   }
   const int tiles_m = (m + BM - 1) / BM;
   const int tiles_n = (n + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(64 * (WM * WN + NP)), lds_bytes, st, xq, s_x, wq, s_w,
-                     bias, m, n, k, tiles_m, tiles_n, y, acc);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(64 * (WM * WN + NP)), lds_bytes, st, xq,
+                     s_x, wq, s_w, bias, m, n, k, tiles_m, tiles_n, nx, y, acc);
   return hipGetLastError();
 }
 
@@ -470,7 +471,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 // (relative; the operand stream per CU bounds every tile, so a round's
 // duration follows the tile's operand bytes and its L2 behaviour). The
 // 384 x 192 tile exists for K % 128 == 0 only.
-TileCfg choose_tile(int64_t m, int64_t n, int64_t k) {
+TileCfg choose_tile(int64_t m, int64_t n, int64_t k, int cus) {
   const TileCfg cands[] = {{384, 192, 2, 1}, {256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
   // duration of one full round relative to the 192 tile's (4608-row layers)
   const double round_t[] = {1.75, 1.336, 1.0, 1.0};
@@ -480,11 +481,11 @@ TileCfg choose_tile(int64_t m, int64_t n, int64_t k) {
     const TileCfg& t = cands[c];
     if (t.bm == 384 && k % 128 != 0) continue;
     const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
-    const int64_t slots = 256LL * t.per_cu;
+    const int64_t slots = (int64_t)(cus > 0 ? cus : 1) * t.per_cu;
     const int64_t rounds = (tiles + slots - 1) / slots;
     // with no more 128 tiles than CUs each block runs alone on its CU:
     // measured 0.92 of the 192 tile's one-round time (1024x3840x3840)
-    const double rt = (t.per_cu == 2 && tiles <= 256) ? 0.92 : round_t[c];
+    const double rt = (t.per_cu == 2 && tiles <= cus) ? 0.92 : round_t[c];
     const double time = (double)rounds * rt;
     if (time < best_t * 0.999) {
       best_t = time;
@@ -504,24 +505,24 @@ TileCfg choose_tile(int64_t m, int64_t n, int64_t k) {
 template <bool PC, bool F16>
 static hipError_t launch_tile(int tile, const int8_t* xq, const float* s_x, const int8_t* wq,
                               const float* s_w, const uint16_t* bias, int M, int N, int K,
-                              uint16_t* y, int32_t* acc, hipStream_t st) {
+                              uint16_t* y, int32_t* acc, int nx, hipStream_t st) {
   switch (tile) {
     case 256:
       if (K % 128 == 0)
-        return launch_cfg<PC, F16, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<PC, F16, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, F16, 256, 256, 128, 2, 4, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
+      return launch_cfg<PC, F16, 256, 256, 64, 2, 4, 4, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
     case 384:  // 384 x 192 (K % 128 == 0 only)
       return launch_cfg<PC, F16, 384, 192, 128, 4, 2, 2, 1>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
-                                                            st);
+                                                            nx, st);
     case 192:
       if (K % 128 == 0)
         return launch_cfg<PC, F16, 192, 192, 128, 2, 2, 3, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc,
-                                                          st);
-      return launch_cfg<PC, F16, 192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+                                                          nx, st);
+      return launch_cfg<PC, F16, 192, 192, 64, 2, 2, 6, 1, 4>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
     default:
       if (K % 128 == 0)
-        return launch_cfg<PC, F16, 128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
-      return launch_cfg<PC, F16, 128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+        return launch_cfg<PC, F16, 128, 128, 128, 2, 2, 2, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
+      return launch_cfg<PC, F16, 128, 128, 64, 2, 2, 4, 2>(xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
   }
 }
 
@@ -531,20 +532,33 @@ hipError_t launch_gemm(const int8_t* xq, const float* s_x, const int8_t* wq, con
   return launch_gemm_tile(xq, s_x, wq, s_w, sw_per_channel, bias, m, n, k, y, acc, 0, dt, st);
 }
 
+LaunchPlan plan_gemm(int64_t m, int64_t n, int64_t k, int tile, int cus) {
+  LaunchPlan p;
+  if (tile == 0) tile = choose_tile(m, n, k, cus).bm;
+  p.tile_m = tile;
+  p.tile_n = tile == 384 ? 192 : tile;
+  p.block = tile == 192 ? 512 : (tile == 128 ? 256 : 512);
+  p.grid = ((m + p.tile_m - 1) / p.tile_m) * ((n + p.tile_n - 1) / p.tile_n);
+  p.xcds = xcd_count(cus);
+  p.passes = 1;
+  return p;
+}
+
 hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq,
                             const float* s_w, bool sw_per_channel, const uint16_t* bias,
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int32_t* acc, int tile,
                             DType dt, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (tile == 0) tile = choose_tile(m, n, k).bm;
-  const int M = (int)m, N = (int)n, K = (int)k;
+  const int cus = compute_units();
+  const LaunchPlan p = plan_gemm(m, n, k, tile, cus);
+  const int M = (int)m, N = (int)n, K = (int)k, nx = p.xcds;
   if (dt == DType::kF16)
     return sw_per_channel
-               ? launch_tile<true, true>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st)
-               : launch_tile<false, true>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+               ? launch_tile<true, true>(p.tile_m, xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st)
+               : launch_tile<false, true>(p.tile_m, xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
   return sw_per_channel
-             ? launch_tile<true, false>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st)
-             : launch_tile<false, false>(tile, xq, s_x, wq, s_w, bias, M, N, K, y, acc, st);
+             ? launch_tile<true, false>(p.tile_m, xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st)
+             : launch_tile<false, false>(p.tile_m, xq, s_x, wq, s_w, bias, M, N, K, y, acc, nx, st);
 }
 
 }  // namespace convrot

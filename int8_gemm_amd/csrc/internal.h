@@ -8,6 +8,28 @@ namespace convrot {
 // 16-bit float format of activations, bias and outputs.
 enum class DType { kBF16 = 0, kF16 = 1 };
 
+// Compute units that launches size their grids for: the current device's
+// count (queried once per device), or the process-wide override of
+// convrot_set_compute_units.
+int compute_units();
+
+// Launch geometry of a kernel (host-side sizing, testable without a GPU).
+struct LaunchPlan {
+  int64_t grid = 0;        // workgroups
+  int block = 0;           // threads per workgroup
+  int rows_per_block = 0;  // rows of a batch (act-quant) / 32-row tiles per step (dequant)
+  int tile_m = 0, tile_n = 0;  // GEMM block tile
+  int xcds = 1;            // XCDs the GEMM's tile order spreads over
+  int64_t passes = 0;      // batches per workgroup of a persistent grid (ceil)
+};
+// Act-quant fast kernel (deferred = false) or its deferred-row pass.
+LaunchPlan plan_act_quant(int64_t rows, int K, bool deferred, int cus);
+// Exact kernel over every row (weight quantization and the exact entry point).
+LaunchPlan plan_exact(int64_t rows, int K, int cus);
+LaunchPlan plan_dequant(int64_t n, int64_t k, int g, int cus);
+// tile 0 = automatic choice
+LaunchPlan plan_gemm(int64_t m, int64_t n, int64_t k, int tile, int cus);
+
 // Rotate + quantize rows (per-row scales): fast kernel, then the exact kernel
 // over the rows it deferred (bf16 only: half rows are never deferred).
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,

@@ -720,19 +720,31 @@ TeamShape team_shape(int T, int wpc) {
 #endif
 constexpr int kFastWavesPerCU = CONVROT_FAST_WAVES_PER_CU;
 
+// Grid of a persistent rotate kernel: blocks of whole rows of T lanes, as
+// many as stay resident together at `wpc` waves per CU (a grid beyond that
+// would run a second, partial round of blocks), no more than there are
+// batches.
+LaunchPlan plan_rotate(int64_t rows, int T, int wpc, int cus) {
+  const TeamShape ts = team_shape(T, wpc);
+  LaunchPlan p;
+  p.block = ts.block;
+  p.rows_per_block = ts.rpb;
+  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
+  const int per_cu = wpc / (ts.block / 64);
+  const int64_t cap = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  p.grid = nbatches < cap ? nbatches : cap;
+  p.passes = p.grid > 0 ? (nbatches + p.grid - 1) / p.grid : 0;
+  return p;
+}
+
 template <int G>
 hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
                        const SignMask& sm, bool f16, hipStream_t st) {
-  const TeamShape ts = team_shape(K / 64, kFastWavesPerCU);
-  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
-  // whole blocks per CU that stay resident together: a grid beyond that would
-  // run a second, partial round of blocks
-  const int per_cu = kFastWavesPerCU / (ts.block / 64);
-  const int64_t cap = (int64_t)kNumCUs * (per_cu > 0 ? per_cu : 1);
-  const int64_t blocks = nbatches < cap ? nbatches : cap;
+  const LaunchPlan p = plan_act_quant(rows, K, false, compute_units());
+  const int64_t nbatches = (rows + p.rows_per_block - 1) / p.rows_per_block;
   auto kern = f16 ? rotate_quant_fast_kernel<G, true> : rotate_quant_fast_kernel<G, false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ts.block), 0, st, x, xq, s, rows, K,
-                     ts.T, ts.rpb, nbatches, sm);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(p.block), 0, st, x, xq, s, rows, K,
+                     K / 64, p.rows_per_block, nbatches, sm);
   return hipGetLastError();
 }
 
@@ -750,21 +762,27 @@ constexpr int kDeferredWavesPerCU = CONVROT_DEFERRED_WAVES_PER_CU;
 template <int G>
 hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tensor_amax,
                         int64_t rows, int K, const SignMask& sm, int mode, hipStream_t st) {
-  const int wpc = mode == kRowDeferred ? kDeferredWavesPerCU : kExactWavesPerCU;
-  const TeamShape ts = team_shape(K / 32, wpc);
-  const int64_t nbatches = (rows + ts.rpb - 1) / ts.rpb;
-  const int per_cu = wpc / (ts.block / 64);  // whole resident blocks per CU
-  const int64_t cap = (int64_t)kNumCUs * (per_cu > 0 ? per_cu : 1);
-  const int64_t blocks = nbatches < cap ? nbatches : cap;
+  const LaunchPlan p = mode == kRowDeferred ? plan_act_quant(rows, K, true, compute_units())
+                                            : plan_exact(rows, K, compute_units());
+  const int64_t nbatches = (rows + p.rows_per_block - 1) / p.rows_per_block;
   // rows the fast kernel left get a rounded float64 transform first
   auto kern = mode == kRowDeferred ? rotate_quant_exact_kernel<G, true>
                                    : rotate_quant_exact_kernel<G, false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ts.block), 0, st, x, xq, s, tensor_amax,
-                     rows, K, ts.T, ts.rpb, nbatches, sm, mode);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(p.block), 0, st, x, xq, s, tensor_amax,
+                     rows, K, K / 32, p.rows_per_block, nbatches, sm, mode);
   return hipGetLastError();
 }
 
 }  // namespace
+
+LaunchPlan plan_act_quant(int64_t rows, int K, bool deferred, int cus) {
+  return deferred ? plan_rotate(rows, K / 32, kDeferredWavesPerCU, cus)
+                  : plan_rotate(rows, K / 64, kFastWavesPerCU, cus);
+}
+
+LaunchPlan plan_exact(int64_t rows, int K, int cus) {
+  return plan_rotate(rows, K / 32, kExactWavesPerCU, cus);
+}
 
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
                                 int g, const SignMask& sm, DType dt, hipStream_t st) {

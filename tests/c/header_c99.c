@@ -52,6 +52,12 @@ int convrot_header_c99_check(void* p, int i) {
     (void)convrot_linear_int8_workspace_size(1, 16, 64);
     (void)convrot_status_string(CONVROT_E_SELFCHECK);
     (void)convrot_last_error_string();
+    {
+      convrot_launch_plan plan;
+      s = convrot_plan_launch(CONVROT_KERNEL_GEMM, 1, 16, 64, 4, 256, &plan);
+      s = convrot_set_compute_units(0);
+      tile += (int)plan.grid + convrot_compute_units();
+    }
   }
   return (int)s + convrot_abi_version() + (int)CONVROT_ABI_VERSION + tile + latched + (int)err;
 }

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 5
+    assert cr.convrot_abi_version() == 6
     for s in range(8):
         assert cr.convrot_status_string(s)
     assert cr.convrot_status_string(7).startswith("first-call check")
@@ -269,3 +269,60 @@ def test_header_compiles_and_links_as_c99(lib, tmp_path):
                         "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+# --------------------------------------------------------------------------
+# Launch sizing from the device's compute units (host only)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cus", [256, 128, 64, 32, 3])
+def test_launch_plans_follow_compute_units(lib, cus):
+    """Persistent grids hold at most a fixed number of workgroups per CU, the
+    GEMM's tile order spreads over CUs / 32 XCDs, and a plan covers the shape."""
+    # act-quant at K = 3840: one 60-lane row per 1-wave block, 8 per CU
+    p = cr.convrot_plan_launch("act_quant", m=4608, k=3840, g=256, compute_units=cus)
+    assert p["compute_units"] == cus and p["block"] == 64 and p["rows_per_block"] == 1
+    assert p["grid"] == min(4608, 8 * cus)
+    assert p["grid"] * p["passes"] >= 4608 > p["grid"] * (p["passes"] - 1)
+    # deferred rows at K = 12288: 6-wave rows, one block per CU
+    p = cr.convrot_plan_launch("act_quant_deferred", m=4608, k=12288, g=256, compute_units=cus)
+    assert p["block"] == 384 and p["grid"] == min(4608, cus)
+    # dequant: 2 blocks per CU at g = 256, 4 at g <= 64
+    for g, per_cu in ((256, 2), (64, 4), (4, 4)):
+        p = cr.convrot_plan_launch("dequant", n=3840, k=3840, g=g, compute_units=cus)
+        tiles = 3840 * 3840 // max(g, 32) // 32
+        steps = tiles if g == 256 else tiles // 4
+        assert p["grid"] == min(steps, per_cu * cus), g
+        assert p["grid"] * p["passes"] >= steps
+    # GEMM: a tile that covers the output, the XCD count of the tile order
+    p = cr.convrot_plan_launch("gemm", m=32760, n=13824, k=5120, compute_units=cus)
+    assert p["xcds"] == (cus // 32 if cus >= 64 else 1)
+    tm, tn = p["tile_m"], p["tile_n"]
+    assert p["grid"] == -(-32760 // tm) * -(-13824 // tn)
+
+
+def test_gemm_tile_choice_counts_rounds_over_the_cus(lib):
+    """The 384 x 192 tile covers 4608 x 3840 in 240 tiles, one round on 256
+    CUs; on 128 CUs that takes two rounds, where the 256 x 256 tile's 270
+    tiles take three and the 192 tile's 480 four (a 384 x 192 round lasts 1.75
+    of a 192 round, a 256 round 1.336): the 384 tile stays the choice."""
+    for cus in (256, 128):
+        p = cr.convrot_plan_launch("gemm", m=4608, n=3840, k=3840, compute_units=cus)
+        assert (p["tile_m"], p["tile_n"], p["grid"]) == (384, 192, 240), cus
+    # with K % 128 != 0 the 384 tile does not exist
+    p = cr.convrot_plan_launch("gemm", m=4608, n=3840, k=3840 + 64, compute_units=256)
+    assert p["tile_m"] != 384
+    # a single CU: every tile is a round of its own; the fewest-bytes-per-op
+    # tiles win on round count
+    p1 = cr.convrot_plan_launch("gemm", m=4096, n=4096, k=4096, compute_units=1)
+    assert p1["tile_m"] in (256, 384)
+
+
+def test_plan_launch_checks_shapes(lib):
+    with pytest.raises(cr.ConvrotError, match="UNSUPPORTED_GROUP"):
+        cr.convrot_plan_launch("act_quant", m=8, k=96, g=64, compute_units=8)
+    with pytest.raises(cr.ConvrotError, match="UNSUPPORTED_SHAPE"):
+        cr.convrot_plan_launch("gemm", m=8, n=24, k=64, compute_units=8)
+    with pytest.raises(cr.ConvrotError, match="INVALID_ARG"):
+        cr.convrot_set_compute_units(-1)
+    assert cr.convrot_plan_launch("act_quant", m=0, k=256, g=256, compute_units=8)["grid"] == 0

@@ -1,15 +1,20 @@
-"""GPU parity at the full workload shapes, in the launch configurations the
-benchmark times (automatic GEMM tile, convrot_linear_int8 with its default
-workspace, i.e. token slices of at most 2N rows).
+"""GPU parity at the full workload shapes, every output compared, in the
+launch configurations the benchmark times (automatic GEMM tile,
+convrot_linear_int8 with its default workspace, i.e. token slices of at most
+2N rows).
 
-The GPU computes every output. The oracle then recomputes what it can one
-row at a time: the weight quantization in full (it is cheap), and sampled
-weight rows (dequant) and token rows (activation quantization and the whole
-int8 forward). A row's result depends on no other row, so a sampled row is
-the same computation as in the full call. Sampled rows include the first and
-last rows, the rows around GEMM tile edges and around token-slice edges.
-Over all token rows, sampled output columns of the int32 accumulator are
-compared with exact float64 dot products of the GPU's own int8 operands."""
+Per workload (pytest runs all tests of one workload before the next, so the
+GPU results and the oracle's are computed once):
+
+* weight quantization: every element of Wq and s_w;
+* dequant + derotate: every row of W_hat;
+* activation quantization: every row of xq and s_x (the oracle in chunks of
+  4096 token rows; a row's result depends on no other row);
+* the int8 forward: every row and column of y;
+* the GEMM alone: the int32 accumulator at one row of every 128-row band and
+  one column of every 128-column band (so every output tile of every block
+  tile size is hit), and its y at those rows with each forced block tile.
+"""
 
 import numpy as np
 import pytest
@@ -23,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 SEED = synth.ROT_SEED
 DEV = "cuda:0"
+CHUNK = 4096
 
 FULL = [
     (synth.ZIMAGE_ATTN, 256),
@@ -31,12 +37,7 @@ FULL = [
     (synth.WAN_FFN_UP, 256),
     (synth.WAN_FFN_DOWN, 256),
 ] + [(synth.QKV_SWEEP, g) for g in synth.GROUP_SIZES]
-IDS = [f"{layer.name}-g{g}" for layer, g in FULL]
-
-
-@pytest.fixture(scope="module", autouse=True)
-def _lib():
-    cr.load_library()
+IDS = [f"{layer.name.split()[0]}-g{g}" for layer, g in FULL]
 
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
@@ -51,78 +52,115 @@ def f32_bits(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).view(np.uint32)
 
 
-def sample_rows(count: int, extra=(), n_random: int = 8, seed: int = 11) -> np.ndarray:
-    """First/last rows, rows at 128/192/256/384-row tile edges (including the
-    last, ragged tile), the given extra rows and a few random ones."""
-    rows = {0, 1, 127, 128, 191, 192, 255, 256, 383, 384, count - 2, count - 1}
-    for t in (128, 192, 256, 384):
-        last = (count - 1) // t * t
-        rows.update({last - 1, last})
-    rows.update(extra)
-    rows.update(np.random.default_rng(seed).integers(0, count, n_random).tolist())
-    return np.array(sorted(r for r in rows if 0 <= r < count))
+def band_samples(count: int, band: int = 128, salt: int = 37) -> np.ndarray:
+    """One index in every band of `band` indices (its offset varies from band
+    to band), plus the first and the last index."""
+    idx = {0, count - 1}
+    for b in range((count + band - 1) // band):
+        lo, hi = b * band, min(count, (b + 1) * band)
+        idx.add(lo + (b * salt + 5) % (hi - lo))
+    return np.array(sorted(idx))
 
 
-@pytest.mark.parametrize("layer,g", FULL, ids=IDS)
-def test_fullsize(layer, g):
-    m, n, k = layer.m, layer.n, layer.k
-    print(f"full-size {layer.name} g={g}: inputs", flush=True)
-    wb, xb = layer.w(), layer.x()
+class Workload:
+    """GPU results and oracle results of one workload, filled test by test."""
 
-    # weight quantization: every element, bit-exact
-    print(f"full-size {layer.name} g={g}: quantize_weights", flush=True)
-    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
-    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    def __init__(self, layer, g):
+        self.layer, self.g = layer, g
+        self.name = f"{layer.name} g={g}"
+
+
+@pytest.fixture(scope="module", params=FULL, ids=IDS)
+def wl(request):
+    cr.load_library()
+    w = Workload(*request.param)
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def _say(wl, what):
+    print(f"full-size {wl.name}: {what}", flush=True)
+
+
+def test_weights_every_element(wl):
+    _say(wl, "quantize_weights")
+    wb = wl.layer.w()
+    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), wl.g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights(wb, wl.g, SEED)
     assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
     assert np.array_equal(wq.cpu().numpy(), wq_ref)
-    del wb
+    wl.wq, wl.s_w, wl.wq_ref, wl.s_ref = wq, s_w, wq_ref, s_ref
 
-    # dequant + derotate: sampled weight rows, bit-exact
-    print(f"full-size {layer.name} g={g}: dequant", flush=True)
-    w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
-    nrows = sample_rows(n)
-    assert np.array_equal(host_bits(w_hat[torch.from_numpy(nrows).to(DEV)]),
-                          oracle.dequant_derotate(wq_ref[nrows], s_ref, g, SEED))
+
+def test_dequant_every_row(wl):
+    _say(wl, "dequant")
+    w_hat = cr.convrot_dequant_derotate(wl.wq, wl.s_w, wl.g, SEED)
+    n = wl.layer.n
+    step = max(1, (CHUNK * 4096) // wl.layer.k)
+    for r0 in range(0, n, step):
+        want = oracle.dequant_derotate(wl.wq_ref[r0:r0 + step], wl.s_ref, wl.g, SEED)
+        assert np.array_equal(host_bits(w_hat[r0:r0 + step]), want), f"weight rows {r0}.."
     del w_hat
 
-    # activations: sampled token rows, bit-exact
-    print(f"full-size {layer.name} g={g}: quantize_activations", flush=True)
+
+def test_act_quant_every_row(wl):
+    _say(wl, "quantize_activations")
+    xb = wl.layer.x()
     x = dev_bf16(xb)
-    xq, s_x = cr.convrot_quantize_activations(x, g, SEED)
-    slice_rows = 2 * n  # default workspace slices tokens at most 2N rows high
-    rows = sample_rows(m, extra=(slice_rows - 1, slice_rows, 2 * slice_rows - 1, 2 * slice_rows))
-    rows_t = torch.from_numpy(rows).to(DEV)
-    xq_ref, sx_ref = oracle.quantize_activations(xb[rows], g, SEED)
-    assert np.array_equal(f32_bits(s_x[rows_t].cpu().numpy()), f32_bits(sx_ref))
-    assert np.array_equal(xq[rows_t].cpu().numpy(), xq_ref)
+    xq, s_x = cr.convrot_quantize_activations(x, wl.g, SEED)
+    xq_h, sx_h = xq.cpu().numpy(), s_x.cpu().numpy()
+    xq_ref = np.empty_like(xq_h)
+    sx_ref = np.empty_like(sx_h)
+    for r0 in range(0, wl.layer.m, CHUNK):
+        xq_ref[r0:r0 + CHUNK], sx_ref[r0:r0 + CHUNK] = oracle.quantize_activations(
+            xb[r0:r0 + CHUNK], wl.g, SEED)
+        assert np.array_equal(f32_bits(sx_h[r0:r0 + CHUNK]), f32_bits(sx_ref[r0:r0 + CHUNK])), \
+            f"s_x rows {r0}.."
+        assert np.array_equal(xq_h[r0:r0 + CHUNK], xq_ref[r0:r0 + CHUNK]), f"xq rows {r0}.."
+    wl.x, wl.xq, wl.s_x, wl.xq_ref, wl.sx_ref = x, xq, s_x, xq_ref, sx_ref
 
-    # the int8 forward with the default workspace: sampled rows, every column
-    print(f"full-size {layer.name} g={g}: linear_int8", flush=True)
-    y = cr.convrot_linear_int8(x, wq, s_w, g, SEED)
-    y_ref = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref)
-    assert np.array_equal(host_bits(y[rows_t]), y_ref)
-    del x, y
 
-    # the GEMM over every token row: sampled accumulator columns, exact
-    print(f"full-size {layer.name} g={g}: gemm columns", flush=True)
-    y2, acc = cr.convrot_gemm_int8(xq, s_x, wq, s_w, want_acc=True)
-    cols = sample_rows(n, n_random=4)
-    cols_t = torch.from_numpy(cols).to(DEV)
-    got = acc[:, cols_t].cpu().numpy()
-    wcols = wq_ref[cols].astype(np.float64).T
-    for r0 in range(0, m, 4096):  # exact: integer partial sums below 2^53
-        want = xq[r0:r0 + 4096].cpu().numpy().astype(np.float64) @ wcols
-        assert np.array_equal(got[r0:r0 + 4096], want.astype(np.int64)), f"rows {r0}.."
-    # and the epilogue of the same launch on those columns, at the sampled
-    # token rows (oracle operands only)
-    y_cols = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref[cols]), s_ref, sx_ref)
-    assert np.array_equal(host_bits(y2[rows_t][:, cols_t].contiguous()), y_cols)
+def _oracle_y(wl, r0, r1):
+    acc = oracle.gemm_int32(wl.xq_ref[r0:r1], wl.wq_ref)
+    return oracle.epilogue(acc, wl.s_ref, wl.sx_ref[r0:r1])
+
+
+def test_linear_every_row(wl):
+    _say(wl, "linear_int8 (default workspace)")
+    y = cr.convrot_linear_int8(wl.x, wl.wq, wl.s_w, wl.g, SEED)
+    step = max(256, (CHUNK * 4096) // wl.layer.n)
+    for r0 in range(0, wl.layer.m, step):
+        assert np.array_equal(host_bits(y[r0:r0 + step]), _oracle_y(wl, r0, r0 + step)), \
+            f"y rows {r0}.."
+    del y
+
+
+def test_gemm_every_tile(wl):
+    _say(wl, "gemm: accumulator at every 128-band, y at those rows per tile")
+    m, n = wl.layer.m, wl.layer.n
+    rows, cols = band_samples(m), band_samples(n, salt=53)
+    rows_t, cols_t = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+    y_want = oracle.epilogue(oracle.gemm_int32(wl.xq_ref[rows], wl.wq_ref), wl.s_ref,
+                             wl.sx_ref[rows])
+    acc_want = oracle.gemm_int32(wl.xq_ref[rows], wl.wq_ref[cols])
+    y, acc = cr.convrot_gemm_int8(wl.xq, wl.s_x, wl.wq, wl.s_w, want_acc=True)
+    assert np.array_equal(acc[rows_t][:, cols_t].cpu().numpy(), acc_want)
+    assert np.array_equal(host_bits(y[rows_t]), y_want)
+    del acc
+    for tile in (128, 192, 256, 384):
+        if tile == 384 and wl.layer.k % 128:
+            continue
+        y, _ = cr.convrot_gemm_int8(wl.xq, wl.s_x, wl.wq, wl.s_w, y=y, tile=tile)
+        assert np.array_equal(host_bits(y[rows_t]), y_want), tile
+    del y
 
 
 def test_dequant_stack_layers_0_and_59():
     """The streamed stack: each stack weight quantized once and copied into 60
     distinct device buffers; layers 0 and 59 dequantize bit-exactly (the same
     launch the benchmark's stack pass makes, per buffer)."""
+    cr.load_library()
     g = 256
     for lay in (synth.STACK_SQUARE, synth.STACK_WIDE):
         print(f"dequant stack {lay.name}", flush=True)
@@ -139,11 +177,11 @@ def test_dequant_stack_layers_0_and_59():
 
 
 def test_fullsize_per_channel_zimage_attn():
-    """Per-channel scales at the full Z-Image attention shape: the weight
-    quantization in full, the dequant on sampled weight rows, the int8 forward
-    on sampled token rows, every column."""
+    """Per-channel scales at the full Z-Image attention shape, every output:
+    the weight quantization, the dequant, the int8 forward."""
+    cr.load_library()
     layer, g = synth.ZIMAGE_ATTN, 256
-    m, n = layer.m, layer.n
+    n = layer.n
     print(f"full-size per-channel {layer.name}: quantize_weights", flush=True)
     e = np.random.default_rng(5).integers(-12, 13, n)
     wb = synth.f32_to_bf16_bits((oracle.bf16_to_f64(layer.w()) * 2.0 ** e[:, None])
@@ -154,16 +192,13 @@ def test_fullsize_per_channel_zimage_attn():
     assert np.array_equal(wq.cpu().numpy(), wq_ref)
 
     print(f"full-size per-channel {layer.name}: dequant", flush=True)
-    nrows = sample_rows(n, n_random=24)
     w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
-    assert np.array_equal(host_bits(w_hat[torch.from_numpy(nrows).to(DEV)]),
-                          oracle.dequant_derotate(wq_ref[nrows], s_ref[nrows], g, SEED))
+    assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
     del w_hat
 
     print(f"full-size per-channel {layer.name}: linear_int8", flush=True)
     xb = layer.x()
     y = cr.convrot_linear_int8_per_channel(dev_bf16(xb), wq, s_w, g, SEED)
-    rows = sample_rows(m, extra=(2 * n - 1, 2 * n))
-    xq_ref, sx_ref = oracle.quantize_activations(xb[rows], g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
     y_ref = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref)
-    assert np.array_equal(host_bits(y[torch.from_numpy(rows).to(DEV)]), y_ref)
+    assert np.array_equal(host_bits(y), y_ref)

@@ -1,0 +1,159 @@
+"""Every pass of the persistent grids against the oracle, element by element.
+
+The act-quant kernels (fast and deferred-row), the exact kernel and the
+dequant walk their work in persistent workgroups, each taking batch i,
+i + grid, i + 2 grid, ... with the next batch prefetched into registers and
+per-batch LDS slots used round-robin. At the reduced test shapes one pass
+covers everything, so:
+
+* the first tests shrink the grids through convrot_set_compute_units (a
+  process-wide test hook; sizing changes speed, never results) until every
+  workgroup walks many batches, and compare every output with the oracle;
+* the last tests use the device's own grid at shapes large enough for
+  several passes (checked with convrot_plan_launch), compared in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_gemm_amd as cr
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = synth.ROT_SEED
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    cr.load_library()
+    yield
+    cr.convrot_set_compute_units(0)
+
+
+@pytest.fixture
+def few_cus(request):
+    cr.convrot_set_compute_units(request.param)
+    yield request.param
+    cr.convrot_set_compute_units(0)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+CASES = [
+    (synth.ZIMAGE_ATTN.scaled(m=300, n=272), 256),
+    (synth.FLUX_MLP_DOWN.scaled(m=40, n=256), 256),   # GELU tails: deferred rows
+    (synth.WAN_FFN_UP.scaled(m=130, n=400), 256),
+    (synth.QKV_SWEEP.scaled(m=260, n=288), 4),
+    (synth.QKV_SWEEP.scaled(m=260, n=288), 16),
+    (synth.QKV_SWEEP.scaled(m=260, n=288), 64),
+]
+IDS = [f"{l.name}-g{g}" for l, g in CASES]
+
+
+@pytest.mark.parametrize("few_cus", [1, 3], indirect=True)
+@pytest.mark.parametrize("layer,g", CASES, ids=IDS)
+def test_small_grids_every_output(few_cus, layer, g):
+    m, n, k = layer.m, layer.n, layer.k
+    plans = {kern: cr.convrot_plan_launch(kern, m=m, n=n, k=k, g=g)
+             for kern in ("act_quant", "act_quant_deferred", "exact")}
+    plans["dequant"] = cr.convrot_plan_launch("dequant", n=n, k=k, g=g)
+    assert all(p["compute_units"] == few_cus for p in plans.values())
+    print(f"multipass cus={few_cus} {layer.name} g={g}: passes "
+          + ", ".join(f"{kk} {p['passes']}" for kk, p in plans.items()), flush=True)
+    assert plans["act_quant"]["passes"] >= 4 and plans["exact"]["passes"] >= 4
+    xb, wb = layer.x(), layer.w()
+    # weights: exact kernel, two per-tensor passes over every row
+    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    # dequant
+    w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
+    assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+    # activations: fast kernel + deferred pass, and the exact kernel alone
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
+    x = dev_bf16(xb)
+    for fn in (cr.convrot_quantize_activations, cr.convrot_quantize_activations_exact):
+        xq, sx = fn(x, g, SEED)
+        assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref)), fn.__name__
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), fn.__name__
+    # the forward (its GEMM tile chosen for the small CU count)
+    y = cr.convrot_linear_int8(x, wq, s_w, g, SEED)
+    acc_ref = oracle.gemm_int32(xq_ref, wq_ref)
+    assert np.array_equal(host_bits(y), oracle.epilogue(acc_ref, s_ref, sx_ref))
+
+
+@pytest.mark.parametrize("few_cus", [2], indirect=True)
+def test_small_grids_per_channel_and_f16(few_cus):
+    layer, g = synth.ZIMAGE_ATTN.scaled(m=200, n=256), 256
+    xb, wb = layer.x(), layer.w()
+    wq, s_w = cr.convrot_quantize_weights_per_channel(dev_bf16(wb), g, SEED)
+    wq_ref, s_ref = oracle.quantize_weights_per_channel(wb, g, SEED)
+    assert np.array_equal(f32_bits(s_w.cpu().numpy()), f32_bits(s_ref))
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
+    assert np.array_equal(host_bits(w_hat), oracle.dequant_derotate(wq_ref, s_ref, g, SEED))
+    hb = layer.x(fmt="f16")
+    xh = torch.from_numpy(hb.view(np.int16)).view(torch.float16).to(DEV)
+    xq, sx = cr.convrot_quantize_activations_ex(xh, g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(hb, g, SEED, dtype="f16")
+    assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    y = cr.convrot_linear_int8_ex(xh, wq, s_w, g, SEED, per_channel=True)
+    want = oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref, dtype="f16")
+    assert np.array_equal(host_bits(y), want)
+
+
+def _device_passes(kern, **shape):
+    return cr.convrot_plan_launch(kern, **shape)["passes"]
+
+
+def test_device_grid_fast_kernel_several_passes():
+    """6200 token rows at K = 3840: one row per 1-wave block, so the device's
+    grid walks each block over several rows (register prefetch of the next
+    row, three LDS slots in rotation); every row compared."""
+    layer, g = synth.ZIMAGE_ATTN.scaled(m=6200, n=256), 256
+    passes = _device_passes("act_quant", m=layer.m, k=layer.k, g=g)
+    print(f"device grid: act-quant 6200x3840 passes {passes}", flush=True)
+    assert passes >= 3
+    xb = layer.x()
+    xq, sx = cr.convrot_quantize_activations(dev_bf16(xb), g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
+    assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+def test_device_grid_deferred_pass_several_passes():
+    """GELU-tailed rows at K = 12288 are deferred by the fast kernel; 1100 of
+    them make the deferred-row pass walk several batches per workgroup on the
+    device's grid; every row compared, and the forward on every row."""
+    layer, g = synth.FLUX_MLP_DOWN.scaled(m=1100, n=256), 256
+    passes = _device_passes("act_quant_deferred", m=layer.m, k=layer.k, g=g)
+    print(f"device grid: deferred 1100x12288 passes {passes}", flush=True)
+    assert passes >= 3
+    xb, wb = layer.x(), layer.w()
+    x = dev_bf16(xb)
+    xq, sx = cr.convrot_quantize_activations(x, g, SEED)
+    xq_ref, sx_ref = oracle.quantize_activations(xb, g, SEED)
+    assert np.array_equal(f32_bits(sx.cpu().numpy()), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    wq = torch.from_numpy(wq_ref).to(DEV)
+    s_w = torch.tensor([s_ref], dtype=torch.float32, device=DEV)
+    y = cr.convrot_linear_int8(x, wq, s_w, g, SEED)
+    assert np.array_equal(host_bits(y),
+                          oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref))

@@ -46,6 +46,15 @@ def _announce(msg):
     print(msg, flush=True)
 
 
+def bf16_matmul_nt(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """y = x . w^T in x's 16-bit format (torch's hipBLASLt matmul): the
+    caller's consumer of the dequantized weight. The transposed operand is
+    made contiguous first, so the product is a plain 2-D matmul of
+    contiguous operands."""
+    assert x.dtype == w.dtype and x.dtype in (torch.bfloat16, torch.float16)
+    return torch.matmul(x, w.t().contiguous())
+
+
 # reduced shapes spanning several GEMM tiles and ragged tails, with each
 # workload's K and value recipe
 REDUCED = [
@@ -129,10 +138,14 @@ def test_linear_int8_bitexact_and_tolerances(layer, g):
     yf = oracle.bf16_to_f64(got)
     assert oracle.rel_frobenius(yf, oracle.linear_int8_reference_f64(acc_ref, s_ref, sx_ref)) \
         < 1e-2
-    # the default (dequant) path, consumed by a bf16 matmul
+    # the default (dequant) path as the caller runs it: a bf16 matmul of x
+    # and W_hat (torch on ROCm), against the float64 reference; and the same
+    # product in fp32
     w_hat = cr.convrot_dequant_derotate(wq, s_w, g, SEED)
-    y_deq = (x.float() @ w_hat.float().t()).to(torch.bfloat16)
     ref_deq = oracle.dequant_linear_reference_f64(xb, wq_ref, s_ref, g, SEED)
+    y_bf = bf16_matmul_nt(x, w_hat)
+    assert oracle.rel_frobenius(oracle.bf16_to_f64(host_bits(y_bf)), ref_deq) < 1e-2
+    y_deq = (x.float() @ w_hat.float().t()).to(torch.bfloat16)
     assert oracle.rel_frobenius(oracle.bf16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
 
 
@@ -382,7 +395,7 @@ def test_per_channel_linear_bitexact_and_tolerances(layer, g):
     assert np.array_equal(host_bits(sliced), y_ref)
     # the default path with per-channel scales, consumed by a bf16 matmul
     w_hat = cr.convrot_dequant_derotate_per_channel(wq, s_w, g, SEED)
-    y_deq = (x.float() @ w_hat.float().t()).to(torch.bfloat16)
+    y_deq = bf16_matmul_nt(x, w_hat)
     ref_deq = oracle.dequant_linear_reference_f64(xb, wq_ref, s_ref, g, SEED)
     assert oracle.rel_frobenius(oracle.bf16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
 
@@ -504,8 +517,8 @@ def test_f16_linear_and_dequant(layer, g):
                                                out_dtype=torch.float16)
         assert np.array_equal(host_bits(w_hat),
                               oracle.dequant_derotate(wq_ref, s_ref, g, SEED, "f16"))
-        # the default path in half, consumed by a float32 matmul
-        y_deq = (x.float() @ w_hat.float().t()).to(torch.float16)
+        # the default path in half, consumed by a half matmul
+        y_deq = bf16_matmul_nt(x, w_hat)
         ref_deq = oracle.dequant_linear_reference_f64(hb, wq_ref, s_ref, g, SEED, dtype="f16")
         assert oracle.rel_frobenius(oracle.f16_to_f64(host_bits(y_deq)), ref_deq) < 1e-2
 

@@ -31,16 +31,21 @@ def test_options():
     r = _run("--help")
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--all-configs", "--warm-ms", "--no-cpu-baseline",
-                "--calibrate-copy"):
+                "--calibrate-copy", "--headline-only"):
         assert opt in r.stdout, opt
 
 
 def test_cpu_baseline_fields():
-    res = bench._cpu_baseline(synth.TINY, 256, synth.ROT_SEED, 0.2)
-    assert set(res) == {"value", "unit", "cores", "kind", "sample"}
+    res = bench._cpu_baseline(synth.TINY, 256, synth.ROT_SEED, 0.4)
+    assert {"value", "unit", "cores", "kind", "sample", "stages", "cpu_model", "blas"} <= set(res)
     assert res["kind"] == "oracle" and res["unit"] == "TOPS"
     assert res["value"] > 0 and res["cores"] >= 1
     assert "64x256x256" in res["sample"]
+    st = res["stages"]
+    for key in ("act_quant_GB/s", "dequant_GB/s", "gemm_int32_GOPS", "linear_TOPS"):
+        assert st[key] > 0, key
+    assert st["linear_TOPS"] == res["value"]
+    assert res["cpu_model"] and res["blas"]
 
 
 def test_traffic_only_for_the_current_gemm_source(tmp_path, monkeypatch):

@@ -234,6 +234,29 @@ convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const flo
                                       convrot_dtype dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* The int8 forward of convrot_linear_int8_ex without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The token slices go
+ * through a scratch array of CONVROT_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds per device from its load to the end of the process: slices of
+ * up to floor(64 MiB / (k + 4)) token rows (rounded down to whole 256-row
+ * GEMM tiles; e.g. 13096 rows at k = 5120, 4608 at k = 13824). The call
+ * allocates and frees nothing, and synchronizes nothing.
+ *   x, bias, y, wq, s_w, scale_mode, dtype, m, n, k, g, rot_seed, stream: as
+ *     for convrot_linear_int8_ex; y is bit-identical to its output for every
+ *     workspace size.
+ * Errors as for convrot_linear_int8_ex; CONVROT_E_WORKSPACE if one token row
+ * (k + 4 bytes) would not fit the scratch (never for k <= 16384). The scratch
+ * is shared by every call on a device and keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap in time on one
+ * device race, so callers serialize them (one stream, or stream order). */
+#define CONVROT_NOALLOC_SCRATCH_BYTES (64u << 20)
+convrot_status convrot_linear_int8_noalloc(const void* x, const int8_t* wq, const float* s_w,
+                                           convrot_scale_mode scale_mode, const void* bias,
+                                           int64_t m, int64_t n, int64_t k, int g,
+                                           uint64_t rot_seed, void* y, convrot_dtype dtype,
+                                           void* stream);
+
 /* Host-streamed int8 layers (Invoke docs "int8 Compute": a layer still in
  * system RAM is copied to the GPU as int8 for each step, half the bytes of the
  * unpacked weight, and computed exactly like a resident one; "Memory": the

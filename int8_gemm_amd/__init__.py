@@ -28,7 +28,7 @@ __all__ = [
     "convrot_streamer_linear_int8", "Streamer", "convrot_session_create",
     "convrot_session_destroy", "convrot_session_linear_int8", "convrot_session_lookup",
     "Session", "EXPORTED_SYMBOLS", "convrot_compute_units", "convrot_set_compute_units",
-    "convrot_plan_launch", "KERNELS",
+    "convrot_plan_launch", "KERNELS", "convrot_linear_int8_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -51,8 +51,11 @@ EXPORTED_SYMBOLS = (
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
     "convrot_streamer_linear_int8", "convrot_session_create", "convrot_session_destroy",
     "convrot_session_linear_int8", "convrot_session_lookup", "convrot_compute_units",
-    "convrot_set_compute_units", "convrot_plan_launch",
+    "convrot_set_compute_units", "convrot_plan_launch", "convrot_linear_int8_noalloc",
 )
+
+# bytes of the per-device scratch array behind convrot_linear_int8_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # convrot_kernel values (convrot_plan_launch)
 KERNELS = {"act_quant": 0, "act_quant_deferred": 1, "exact": 2, "dequant": 3, "gemm": 4}
@@ -128,6 +131,7 @@ def load_library():
             "convrot_session_lookup": [P, I64, I64, I64, I, I, I, ctypes.POINTER(I),
                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)],
             "convrot_set_compute_units": [I],
+            "convrot_linear_int8_noalloc": [P, P, P, I, P, I64, I64, I64, I, U64, P, I, P],
             "convrot_plan_launch": [I, I64, I64, I64, I, I, ctypes.POINTER(_LaunchPlan)],
         }
         for name, args in sig.items():
@@ -657,3 +661,27 @@ class Session:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def convrot_linear_int8_noalloc(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor, g: int,
+                                rot_seed: int = ROT_SEED, bias: torch.Tensor | None = None, *,
+                                per_channel: bool = False, out: torch.Tensor | None = None):
+    """convrot_linear_int8_ex without a workspace: the library's per-device
+    scratch array holds the token slices, so the call allocates nothing (pass
+    `out` to allocate nothing on this side either). Calls that overlap in time
+    on one device race on the scratch."""
+    dt = _need16(x, "x", 2)
+    _need(wq, "wq", torch.int8, 2)
+    m, k = x.shape
+    n = wq.shape[0]
+    _need_sw(s_w, per_channel, n)
+    if bias is not None:
+        _need(bias, "bias", x.dtype, 1)
+    out = torch.empty((m, n), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out", x.dtype, 2)
+    _same_device(x, wq, s_w, bias, out)
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_linear_int8_noalloc(_ptr(x), _ptr(wq), _ptr(s_w), mode,
+                                                      _ptr(bias), m, n, k, g, rot_seed,
+                                                      _ptr(out), dt, _stream(x)))
+    return out

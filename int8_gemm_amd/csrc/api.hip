@@ -546,6 +546,90 @@ convrot_status convrot_linear_int8_ex(const void* x, const int8_t* wq, const flo
 }
 
 // ---------------------------------------------------------------------------
+// The int8 forward for callers that cannot allocate: the token slices go
+// through a file-scope device array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+// One slice of int8 activations and their fp32 scales (the workspace layout
+// of convrot_linear_int8). Each device holds its own copy of the array from
+// the library's load to the end of the process.
+static constexpr size_t kScratchBytes = (size_t)CONVROT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// The array's device address per device (the host-side name of a __device__
+// variable is only a stand-in), resolved once with that device current.
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+convrot_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CONVROT_E_INVALID_ARG, "%s: device %d beyond the %d supported", fn, dev,
+                kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, fn);
+      if (!p || !aligned(p, 256))
+        return fail(CONVROT_E_HIP, "%s: scratch address %p unusable", fn, p);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+convrot_status convrot_linear_int8_noalloc(const void* x, const int8_t* wq, const float* s_w,
+                                           convrot_scale_mode scale_mode, const void* bias,
+                                           int64_t m, int64_t n, int64_t k, int g,
+                                           uint64_t rot_seed, void* y, convrot_dtype dtype,
+                                           void* stream) {
+  const char* fn = "convrot_linear_int8_noalloc";
+  bool pc;
+  DType dt;
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d dtype=%d", fn, (int)scale_mode,
+                (int)dtype);
+  // a token row of k int8 plus its scale must fit (always so for k <= 16384)
+  if (k > 0 && convrot_linear_int8_workspace_for_rows(1, k) > kScratchBytes)
+    return fail(CONVROT_E_WORKSPACE, "%s: a row of k=%lld does not fit the %zu-byte scratch", fn,
+                (long long)k, kScratchBytes);
+  // argument checks first (nothing touches HIP when they fail); a stand-in
+  // address of the right alignment lets linear_check size the slices
+  int64_t slice;
+  if (convrot_status st = linear_check(fn, pc, static_cast<const uint16_t*>(x), wq, s_w,
+                                       static_cast<const uint16_t*>(bias), m, n, k, g,
+                                       static_cast<const uint16_t*>(y),
+                                       reinterpret_cast<void*>((uintptr_t)256), kScratchBytes,
+                                       &slice))
+    return st;
+  if (slice == 0) return ok();
+  void* ws = nullptr;
+  if (convrot_status st = scratch_address(fn, &ws)) return st;
+  // the real scratch may not overlap the caller's tensors (it never does:
+  // it is the library's own memory), but check as for a workspace
+  const size_t ny = (size_t)(m * n) * 2;
+  if (overlap(ws, kScratchBytes, y, ny) || overlap(ws, kScratchBytes, x, (size_t)(m * k) * 2))
+    return fail(CONVROT_E_INVALID_ARG, "%s: buffers overlap the scratch", fn);
+  return linear_run(fn, pc, dt, static_cast<const uint16_t*>(x), wq, s_w,
+                    static_cast<const uint16_t*>(bias), m, n, k, g, rot_seed,
+                    static_cast<uint16_t*>(y), ws, slice, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Host-streamed int8 layers: a ring of device staging slots. Each call copies
 // one layer's int8 weight into the next slot on the streamer's own copy
 // stream, and the forward waits for that copy on the caller's stream; the

@@ -57,6 +57,8 @@ int convrot_header_c99_check(void* p, int i) {
       s = convrot_plan_launch(CONVROT_KERNEL_GEMM, 1, 16, 64, 4, 256, &plan);
       s = convrot_set_compute_units(0);
       tile += (int)plan.grid + convrot_compute_units();
+      s = convrot_linear_int8_noalloc(p, q, f, CONVROT_SCALE_PER_TENSOR, p, 1, 16, 64, 4, 1u, p,
+                                      CONVROT_DTYPE_BF16, p);
     }
   }
   return (int)s + convrot_abi_version() + (int)CONVROT_ABI_VERSION + tile + latched + (int)err;

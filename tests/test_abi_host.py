@@ -326,3 +326,18 @@ def test_plan_launch_checks_shapes(lib):
     with pytest.raises(cr.ConvrotError, match="INVALID_ARG"):
         cr.convrot_set_compute_units(-1)
     assert cr.convrot_plan_launch("act_quant", m=0, k=256, g=256, compute_units=8)["grid"] == 0
+
+
+def test_noalloc_argument_checks_without_gpu(lib):
+    """The no-allocation forward checks its arguments before any HIP call,
+    like the workspace forward; m == 0 is a no-op."""
+    P = FAKE
+    fn = lib.convrot_linear_int8_noalloc
+    # bad group, bad shape, null pointers, unknown enums
+    assert fn(P, P, P, 0, None, 8, 16, 96, 64, 1, P, 0, None) == 2
+    assert fn(P, P, P, 0, None, 8, 24, 64, 4, 1, P, 0, None) == 3
+    assert fn(None, P, P, 0, None, 8, 16, 64, 4, 1, P, 0, None) == 1
+    assert fn(P, P, P, 7, None, 8, 16, 64, 4, 1, P, 0, None) == 1
+    assert fn(P, P, P, 0, None, 8, 16, 64, 4, 1, P, 9, None) == 1
+    assert fn(P, P, P, 0, None, 0, 16, 64, 4, 1, P, 0, None) == 0
+    assert cr.NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -257,10 +257,11 @@ convrot_status convrot_linear_int8_noalloc(const void* x, const int8_t* wq, cons
                                            uint64_t rot_seed, void* y, convrot_dtype dtype,
                                            void* stream);
 
-/* Host-streamed int8 layers (Invoke docs "int8 Compute": a layer still in
- * system RAM is copied to the GPU as int8 for each step, half the bytes of the
- * unpacked weight, and computed exactly like a resident one; "Memory": the
- * copy stays within the default path's working memory).
+/* Host-streamed int8 layers (Invoke docs "int8 Compute", the table of a
+ * transformer kept in host memory: a non-resident layer's int8 weight is
+ * moved to the device on every call, at half the bytes of its bf16 form, and
+ * then runs the same forward as a resident layer; "Memory": the staging stays
+ * within the default path's working memory).
  *
  * A convrot_streamer owns `slots` device staging buffers of slot_bytes each, a
  * copy stream of its own (default priority) and two events per slot; it is
@@ -289,10 +290,11 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const vo
                                             size_t workspace_bytes, void* stream);
 
 /* First-call tuning and self-check (Invoke docs "int8 Compute", "Memory" and
- * "When something goes wrong": the first call for each layer shape and
- * token-count bucket tunes the kernels with a cache-sized buffer and is
- * checked against the default path on 256 output rows; on a mismatch or a
- * failing kernel that GPU keeps the default path until restart).
+ * "When something goes wrong": per layer shape and range of token counts, the
+ * kernels are tuned once with a buffer the size of the last-level cache, and
+ * that first output is compared on 256 rows with the dequant path; a
+ * mismatch or a kernel fault sends that GPU back to the dequant path until
+ * the application restarts).
  *
  * A convrot_session (one per device, made on the current device) runs
  * convrot_linear_int8_ex through a table keyed by (n, k, token bucket, g,

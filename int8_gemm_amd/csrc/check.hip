@@ -1,8 +1,8 @@
 // Kernels of the first-call check (Invoke docs "int8 Compute", "Memory" and
-// "When something goes wrong"): the first result for each layer shape and
-// token-count bucket is compared with the default path on up to 256 output
-// rows, and the GEMM tile is tuned after a cache-sized buffer has been
-// written (on MI355X the 256 MB MALL, the largest cache in front of HBM).
+// "When something goes wrong"): once per layer shape and range of token
+// counts, up to 256 output rows of the int8 forward are compared with the
+// dequant path, and the GEMM tile is tuned after a buffer the size of the
+// last-level cache has been written (on MI355X the 256 MB MALL).
 //
 //   ref_rows_kernel:  y_ref[r, c] = sum_k x[r, k] * W_hat[c, k] (+ bias[c]) in
 //                     fp32, W_hat the dequantized (default-path) weight;

@@ -1,8 +1,8 @@
 """GPU: sessions (first-call tile tuning and check against the default path).
 
-The pages check the first result for each layer shape and token-count bucket
-against the default path and keep the default path on that GPU after a
-mismatch (Invoke docs "int8 Compute", "When something goes wrong"). Here:
+On the pages, the int8 forward of each new layer shape and token range is
+compared once with the dequant path, and a mismatch switches that GPU back to
+the dequant path (Invoke docs "int8 Compute", "When something goes wrong"). Here:
 the session's forward equals the plain forward bit for bit whatever tile it
 kept; the check's error equals an independent float64 computation of the
 same quantity from the oracle; a failing check (forced from the host with a

@@ -75,7 +75,69 @@ def _parse():
                          "passes, which time nothing, may set it to 0")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the FFN pair, its legs and the roofline GEMM (profiling runs)")
+    ap.add_argument("--leg", choices=("act_quant", "dequant", "gemm", "linear"),
+                    help="instead of the headline line: time one leg of one workload "
+                         "(--config, --g) over --steps launches (counter and trace runs)")
+    ap.add_argument("--config", default="wan-ffn-up",
+                    help="workload of --leg: " + ", ".join(_CONFIG_NAMES))
+    ap.add_argument("--g", type=int, default=256, help="group size of --leg")
     return ap.parse_args()
+
+
+_CONFIG_NAMES = ("tiny", "zimage-attn", "flux-mlp-up", "flux-mlp-down", "wan-ffn-up",
+                 "wan-ffn-down", "fused-qkv")
+
+
+def _one_leg(args):
+    """One leg of one workload, `args.steps` launches after a warm-up, with the
+    buffers rotated past the MALL; prints one JSON line (HIP-event mean)."""
+    import numpy as np
+    import torch
+
+    import int8_gemm_amd as cr
+    import synth
+    layers = dict(zip(_CONFIG_NAMES, synth.ALL_LAYERS))
+    layer, g, seed = layers[args.config], args.g, synth.ROT_SEED
+    m, n, k = layer.m, layer.n, layer.k
+    cr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wq, s_w = cr.convrot_quantize_weights(to_dev(layer.w()), g, seed)
+    x0 = to_dev(layer.x())
+    if args.leg == "dequant":
+        wqs = _copies(wq, 3 * n * k)
+        outs = _copies(torch.empty((n, k), dtype=torch.bfloat16, device=dev), 3 * n * k)
+        fn = lambda i: cr.convrot_dequant_derotate(wqs[i % len(wqs)], s_w, g, seed,  # noqa: E731
+                                                   out=outs[i % len(outs)])
+        units, unit = 3.0 * n * k + 4.0, "GB/s"
+    else:
+        xs = _copies(x0, 3 * m * k)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sx = torch.empty(m, dtype=torch.float32, device=dev)
+        cr.convrot_quantize_activations(x0, g, seed, xq=xq, s_x=sx)
+        ys = _copies(torch.empty((m, n), dtype=torch.bfloat16, device=dev), 2 * m * n)
+        ws = torch.empty(cr.convrot_linear_int8_workspace_size(m, n, k), dtype=torch.uint8,
+                         device=dev)
+        if args.leg == "act_quant":
+            fn = lambda i: cr.convrot_quantize_activations(  # noqa: E731
+                xs[i % len(xs)], g, seed, xq=xq, s_x=sx)
+            units, unit = 3.0 * m * k + 4.0 * m, "GB/s"
+        elif args.leg == "gemm":
+            fn = lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=ys[i % len(ys)])  # noqa: E731
+            units, unit = 2.0 * m * n * k, "TOPS"
+        else:
+            fn = lambda i: cr.convrot_linear_int8(  # noqa: E731
+                xs[i % len(xs)], wq, s_w, g, seed, workspace=ws, out=ys[i % len(ys)])
+            units, unit = 2.0 * m * n * k, "TOPS"
+    ms = _events_time(fn, max(1, args.steps), stream, batches=1)
+    rate = units / (ms * 1e-3) / (1e12 if unit == "TOPS" else 1e9)
+    print(json.dumps({"leg": args.leg, "config": layer.name, "g": g, "us": round(ms * 1e3, 2),
+                      unit: round(rate, 1)}), flush=True)
 
 
 def _source_hash(path: str) -> str:
@@ -429,6 +491,9 @@ def main():
         sys.exit(2)
     if args.all_configs:
         _all_configs(min(max(args.steps, 10), 50))
+        return
+    if args.leg:
+        _one_leg(args)
         return
 
     import numpy as np

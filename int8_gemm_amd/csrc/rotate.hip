@@ -164,6 +164,14 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   constexpr int KS = LOGG / 2;               // 1/sqrt(g) = 2^-KS
   __shared__ uint32_t s_rowmax[3][256];
   __shared__ uint32_t s_rowflag[3][256];
+  // open elements of wide groups (bf16 only): per row, 1 + the bits of the
+  // largest candidate magnitude, and a flag set when an open element's two
+  // candidates quantize differently (read one batch later); per thread, the
+  // masks of its open elements and of those whose other candidate is the
+  // next float up
+  __shared__ uint32_t s_rowunc[3][F16 ? 1 : 256];
+  __shared__ uint32_t s_rowconf[3][F16 ? 1 : 256];
+  __shared__ uint32_t s_open[F16 ? 1 : 4][F16 ? 1 : 512];
 
   const int tid = threadIdx.x;
   const int r_in = tid / T;
@@ -174,6 +182,10 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     for (int q = 0; q < 3; ++q) {
       s_rowmax[q][tid] = 0u;
       s_rowflag[q][tid] = 0u;
+      if constexpr (!F16) {
+        s_rowunc[q][tid] = 0u;
+        s_rowconf[q][tid] = 0u;
+      }
     }
   }
 
@@ -217,14 +229,18 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   load(batch, w);
   __syncthreads();  // slot initialisation visible
 
-  for (int it = 0; batch < nbatches; ++it, batch += gridDim.x) {
+  int it = 0;
+  for (; batch < nbatches; ++it, batch += gridDim.x) {
     const int64_t row = batch * rows_per_block + r_in;
     const bool active = in_team && row < rows;
     uint32_t wn[32];
     load(batch + gridDim.x, wn);
 
     // ---- exponent span per group (half groups are always exact) ----
-    bool flagged = false;
+    // wide_mask bit gidx: group gidx of this lane spans more binades than the
+    // float64 transform adds exactly; emax_f: the largest exponent field of
+    // those groups
+    uint32_t wide_mask = 0u, emax_f = 0u;
     if constexpr (!F16) {
       constexpr int DW = (G >= CH ? CH : G) / 2;  // dwords per (lane part of a) group
 #pragma unroll
@@ -239,7 +255,10 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
           t = dpp_u32<kQuadXor1>(b); b = b < t ? b : t;
           t = dpp_u32<kQuadXor2>(b); b = b < t ? b : t;
         }
-        flagged |= group_span(a, b) > kMaxSpan;
+        if (group_span(a, b) > kMaxSpan) {
+          wide_mask |= 1u << gidx;
+          emax_f = (a >> 7) > emax_f ? (a >> 7) : emax_f;
+        }
       }
     }
 
@@ -264,29 +283,97 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     // u = RN32(y) (y = unscaled, unsigned sum); x_r = d_j * u * 2^-k for normal x_r
     float u[CH];
     float amax = 0.0f;
+    bool unsafe = false;    // an open element with more than two candidates
+    bool has_open = false;  // this lane holds an open element
+    uint32_t open_hi = 0u;  // bits of the largest candidate magnitude of those
+    if (wide_mask != 0u) {
+      // A wide group's float64 transform is rounded: each output is within
+      // LOGG * 2^-53 * S of the exact sum (a depth-LOGG tree of correctly
+      // rounded additions whose nodes at one level partition the inputs),
+      // S = sum |x| < G * 2^(E+1), E the group's largest exponent. With twice
+      // that bound, delta = 2^(E + ceil(log2 LOGG) + LOGG - 51), the exact
+      // sum lies in [y - delta, y + delta], and since rounding is monotonic
+      // it rounds to RN32(y) when both ends do (the two float64 end points err
+      // by less than the margin). Otherwise the element is open: when the two
+      // ends round to neighbouring floats lo and hi, the exact sum rounds to
+      // one of them and u = RN32(y) is one of them; the row is finished from
+      // u unless an open element's larger candidate could be the row's
+      // absmax, or its two candidates quantize to different bytes (checked
+      // once the scale is known). Wider intervals defer the row.
+      constexpr int LL = LOGG <= 2 ? 1 : (LOGG <= 4 ? 2 : 3);
+      const double delta = __longlong_as_double(
+          (int64_t)(uint64_t)(emax_f + (uint32_t)(1023 - 127 + LL + LOGG - 51)) << 52);
+      uint32_t om[2] = {0u, 0u}, um[2] = {0u, 0u};  // open elements; other candidate above u
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      u[i] = (float)v[i];
-      amax = fmaxf(amax, fabsf(u[i]));
+      for (int i = 0; i < CH; ++i) {
+        u[i] = (float)v[i];
+        amax = fmaxf(amax, fabsf(u[i]));
+        if ((wide_mask >> (i / (G >= CH ? CH : G))) & 1u) {
+          const float lo = (float)(v[i] - delta), hi = (float)(v[i] + delta);
+          if (lo != hi) {
+            // the float right above lo (bit patterns: -0 -> +2^-149)
+            const uint32_t lb = __float_as_uint(lo);
+            const uint32_t nb = lb == 0x80000000u ? 1u : ((lb >> 31) ? lb - 1u : lb + 1u);
+            unsafe |= __uint_as_float(nb) != hi;
+            om[i >> 5] |= 1u << (i & 31);
+            um[i >> 5] |= (u[i] == lo ? 1u : 0u) << (i & 31);
+            const uint32_t mb = __float_as_uint(fmaxf(fabsf(lo), fabsf(hi)));
+            open_hi = mb > open_hi ? mb : open_hi;
+          }
+        }
+      }
+      if (om[0] | om[1]) {
+        has_open = true;
+        s_open[0][tid] = om[0];
+        s_open[1][tid] = om[1];
+        s_open[2][tid] = um[0];
+        s_open[3][tid] = um[1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        u[i] = (float)v[i];
+        amax = fmaxf(amax, fabsf(u[i]));
+      }
     }
 
     const int slot = it % 3;
     if (active) {
       atomicMax(&s_rowmax[slot][r_in], __float_as_uint(amax));
-      if (flagged) atomicOr(&s_rowflag[slot][r_in], 1u);
+      if (unsafe) atomicOr(&s_rowflag[slot][r_in], 1u);
+      if constexpr (!F16) {
+        if (has_open) atomicMax(&s_rowunc[slot][r_in], open_hi + 1u);
+      }
     }
     __syncthreads();
     if (tid < rows_per_block) {
       const int nslot = (it + 2) % 3;
       s_rowmax[nslot][tid] = 0u;
       s_rowflag[nslot][tid] = 0u;
+      if constexpr (!F16) {
+        s_rowunc[nslot][tid] = 0u;
+        s_rowconf[(it + 1) % 3][tid] = 0u;  // read one batch ago, written next batch
+      }
+    }
+    if constexpr (!F16) {
+      // the previous batch's row had an open element whose candidates quantize
+      // differently: defer it (this thread wrote its scale, so the marker
+      // lands after it)
+      const int64_t prev = row - (int64_t)gridDim.x * rows_per_block;
+      if (it > 0 && in_team && c == 0 && prev < rows && s_rowconf[(it + 2) % 3][r_in] != 0u)
+        scale[prev] = __uint_as_float(kDeferredRow);
     }
 
     if (active) {
       const float amax_u = __uint_as_float(s_rowmax[slot][r_in]);
       const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact unless deferred
-      const bool deferred = s_rowflag[slot][r_in] != 0u || !(amax_u <= 3.0e38f) ||
-                            (amax_u > 0.0f && amax_x < 0x1p-100f);
+      bool deferred = s_rowflag[slot][r_in] != 0u || !(amax_u <= 3.0e38f) ||
+                      (amax_u > 0.0f && amax_x < 0x1p-100f);
+      if constexpr (!F16) {
+        // an open element's larger candidate reaches the decided absmax
+        const uint32_t ru = s_rowunc[slot][r_in];
+        deferred |= ru != 0u && ru - 1u >= __float_as_uint(amax_u);
+      }
       if (deferred) {
         if (c == 0) scale[row] = __uint_as_float(kDeferredRow);
       } else {
@@ -322,10 +409,42 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           o[i] = (u4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
+        if constexpr (!F16) {
+          if (has_open) {
+            // both candidates of each open element must give the same byte
+            const uint32_t om0 = s_open[0][tid], om1 = s_open[1][tid];
+            const uint32_t um0 = s_open[2][tid], um1 = s_open[3][tid];
+            bool conflict = false;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+              const uint32_t om = i < 32 ? om0 : om1, um = i < 32 ? um0 : um1;
+              if ((om >> (i & 31)) & 1u) {
+                // the other candidate: the float right above u (um bit set) or
+                // right below it
+                const uint32_t b = __float_as_uint(u[i]);
+                const bool up = (um >> (i & 31)) & 1u;
+                const uint32_t bu = b == 0x80000000u ? 1u : ((b >> 31) ? b - 1u : b + 1u);
+                const uint32_t bd = b == 0u ? 0x80000001u : ((b >> 31) ? b + 1u : b - 1u);
+                const float other = __uint_as_float(up ? bu : bd);
+                const uint32_t q1 = __float_as_uint(u[i] * inv_u + kQuantBias);
+                const uint32_t q2 = __float_as_uint(other * inv_u + kQuantBias);
+                conflict |= ((q1 ^ q2) & 0xFFu) != 0u;
+              }
+            }
+            if (conflict) atomicOr(&s_rowconf[slot][r_in], 1u);
+          }
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) w[i] = wn[i];
+  }
+  if constexpr (!F16) {
+    // conflicts of the last batch
+    __syncthreads();
+    const int64_t last = (batch - gridDim.x) * rows_per_block + r_in;
+    if (it > 0 && in_team && c == 0 && last < rows && s_rowconf[(it - 1) % 3][r_in] != 0u)
+      scale[last] = __uint_as_float(kDeferredRow);
   }
 }
 
@@ -356,22 +475,58 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   const int tid = threadIdx.x;
   const int r_in = tid / T;
   const int c = tid - r_in * T;
-  if (mode == kRowDeferred) {
-    // one parallel look at the scale slots of all rows this block would
-    // visit; usually none is deferred and the block is done
-    bool any = false;
+  // Deferred mode visits only the batches holding a row that the fast kernel
+  // deferred: the scale slots of a chunk of kChunk of this block's batches
+  // are read in one parallel pass into an LDS bitmap (usually empty), whose
+  // marked batches are then taken in order.
+  constexpr int kChunk = 2048;  // 64 words of 32 bits: one per lane of a wave
+  __shared__ uint32_t s_marked[kChunk / 32];
+  int64_t chunk0 = -kChunk;  // first pass of the scanned chunk
+  auto scan_chunk = [&]() {
+    chunk0 += kChunk;
+    __syncthreads();  // earlier readers of the bitmap are done
+    for (int i = tid; i < kChunk / 32; i += blockDim.x) s_marked[i] = 0u;
+    __syncthreads();
     const int64_t per_pass = (int64_t)gridDim.x * rows_per_block;
-    for (int64_t i = tid; ; i += blockDim.x) {
-      const int64_t pass = i / rows_per_block;
-      const int64_t r = (int64_t)blockIdx.x * rows_per_block + pass * per_pass +
-                        (i - pass * rows_per_block);
+    const int64_t base = (int64_t)blockIdx.x * rows_per_block + chunk0 * per_pass;
+    for (int i = tid; i < kChunk * rows_per_block; i += blockDim.x) {
+      const int pass = i / rows_per_block;
+      const int64_t r = base + pass * per_pass + (i - pass * rows_per_block);
       if (r >= rows) break;
-      any |= __float_as_uint(scale[r]) == kDeferredRow;
+      if (__float_as_uint(scale[r]) == kDeferredRow)
+        atomicOr(&s_marked[pass >> 5], 1u << (pass & 31));
     }
-    if (__syncthreads_or(any) == 0) return;
-  }
+    __syncthreads();
+  };
+  // the batch after `batch` to visit (nbatches when none is left); every
+  // thread of the block takes the same steps
+  auto next_batch = [&](int64_t batch) -> int64_t {
+    if (mode != kRowDeferred) return batch + gridDim.x;
+    int64_t pass = batch < 0 ? 0 : (batch - blockIdx.x) / gridDim.x + 1;
+    for (;;) {
+      if (pass >= chunk0 + kChunk) {
+        if (blockIdx.x + (chunk0 + kChunk) * (int64_t)gridDim.x >= nbatches) return nbatches;
+        scan_chunk();
+        pass = chunk0;
+      }
+      // lane l of each wave looks at bitmap word l (kChunk / 32 == 64)
+      const int off = (int)(pass - chunk0);
+      const int lane = tid & 63;
+      uint32_t word = lane < (off >> 5) ? 0u : s_marked[lane];
+      if (lane == (off >> 5)) word &= ~0u << (off & 31);
+      const uint64_t nz = __ballot(word != 0u);
+      if (nz != 0ull) {
+        const int wd = __builtin_ctzll(nz);
+        const uint32_t bits = __shfl(word, wd);
+        const int64_t b = blockIdx.x + (chunk0 + wd * 32 + __builtin_ctz(bits)) * gridDim.x;
+        return b < nbatches ? b : nbatches;
+      }
+      pass = chunk0 + kChunk;
+    }
+  };
   // persistent grid: batches of rows_per_block rows, strided by gridDim.x
-  for (int64_t batch = blockIdx.x; batch < nbatches; batch += gridDim.x) {
+  for (int64_t batch = mode == kRowDeferred ? next_batch(-1) : (int64_t)blockIdx.x;
+       batch < nbatches; batch = next_batch(batch)) {
   __syncthreads();  // the previous batch's readers of the LDS slots are done
   const int64_t row = batch * rows_per_block + r_in;
   bool active = (r_in < rows_per_block) && (row < rows);

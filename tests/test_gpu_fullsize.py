@@ -63,11 +63,31 @@ def band_samples(count: int, band: int = 128, salt: int = 37) -> np.ndarray:
 
 
 class Workload:
-    """GPU results and oracle results of one workload, filled test by test."""
+    """GPU results and oracle results of one workload, computed on first use
+    and kept for the workload's other tests (so any test also runs alone)."""
 
     def __init__(self, layer, g):
         self.layer, self.g = layer, g
         self.name = f"{layer.name} g={g}"
+
+    def weights(self):
+        if not hasattr(self, "wq"):
+            wb = self.layer.w()
+            self.wq, self.s_w = cr.convrot_quantize_weights(dev_bf16(wb), self.g, SEED)
+            self.wq_ref, self.s_ref = oracle.quantize_weights(wb, self.g, SEED)
+        return self
+
+    def activations(self):
+        if not hasattr(self, "xq"):
+            xb = self.layer.x()
+            self.x = dev_bf16(xb)
+            self.xq, self.s_x = cr.convrot_quantize_activations(self.x, self.g, SEED)
+            self.xq_ref = np.empty((self.layer.m, self.layer.k), dtype=np.int8)
+            self.sx_ref = np.empty(self.layer.m, dtype=np.float32)
+            for r0 in range(0, self.layer.m, CHUNK):
+                self.xq_ref[r0:r0 + CHUNK], self.sx_ref[r0:r0 + CHUNK] = \
+                    oracle.quantize_activations(xb[r0:r0 + CHUNK], self.g, SEED)
+        return self
 
 
 @pytest.fixture(scope="module", params=FULL, ids=IDS)
@@ -85,16 +105,14 @@ def _say(wl, what):
 
 def test_weights_every_element(wl):
     _say(wl, "quantize_weights")
-    wb = wl.layer.w()
-    wq, s_w = cr.convrot_quantize_weights(dev_bf16(wb), wl.g, SEED)
-    wq_ref, s_ref = oracle.quantize_weights(wb, wl.g, SEED)
-    assert f32_bits(s_w.cpu().numpy())[0] == f32_bits(s_ref)
-    assert np.array_equal(wq.cpu().numpy(), wq_ref)
-    wl.wq, wl.s_w, wl.wq_ref, wl.s_ref = wq, s_w, wq_ref, s_ref
+    wl.weights()
+    assert f32_bits(wl.s_w.cpu().numpy())[0] == f32_bits(wl.s_ref)
+    assert np.array_equal(wl.wq.cpu().numpy(), wl.wq_ref)
 
 
 def test_dequant_every_row(wl):
     _say(wl, "dequant")
+    wl.weights()
     w_hat = cr.convrot_dequant_derotate(wl.wq, wl.s_w, wl.g, SEED)
     n = wl.layer.n
     step = max(1, (CHUNK * 4096) // wl.layer.k)
@@ -106,19 +124,12 @@ def test_dequant_every_row(wl):
 
 def test_act_quant_every_row(wl):
     _say(wl, "quantize_activations")
-    xb = wl.layer.x()
-    x = dev_bf16(xb)
-    xq, s_x = cr.convrot_quantize_activations(x, wl.g, SEED)
-    xq_h, sx_h = xq.cpu().numpy(), s_x.cpu().numpy()
-    xq_ref = np.empty_like(xq_h)
-    sx_ref = np.empty_like(sx_h)
+    wl.activations()
+    xq_h, sx_h = wl.xq.cpu().numpy(), wl.s_x.cpu().numpy()
     for r0 in range(0, wl.layer.m, CHUNK):
-        xq_ref[r0:r0 + CHUNK], sx_ref[r0:r0 + CHUNK] = oracle.quantize_activations(
-            xb[r0:r0 + CHUNK], wl.g, SEED)
-        assert np.array_equal(f32_bits(sx_h[r0:r0 + CHUNK]), f32_bits(sx_ref[r0:r0 + CHUNK])), \
+        assert np.array_equal(f32_bits(sx_h[r0:r0 + CHUNK]), f32_bits(wl.sx_ref[r0:r0 + CHUNK])), \
             f"s_x rows {r0}.."
-        assert np.array_equal(xq_h[r0:r0 + CHUNK], xq_ref[r0:r0 + CHUNK]), f"xq rows {r0}.."
-    wl.x, wl.xq, wl.s_x, wl.xq_ref, wl.sx_ref = x, xq, s_x, xq_ref, sx_ref
+        assert np.array_equal(xq_h[r0:r0 + CHUNK], wl.xq_ref[r0:r0 + CHUNK]), f"xq rows {r0}.."
 
 
 def _oracle_y(wl, r0, r1):
@@ -128,6 +139,7 @@ def _oracle_y(wl, r0, r1):
 
 def test_linear_every_row(wl):
     _say(wl, "linear_int8 (default workspace)")
+    wl.weights().activations()
     y = cr.convrot_linear_int8(wl.x, wl.wq, wl.s_w, wl.g, SEED)
     step = max(256, (CHUNK * 4096) // wl.layer.n)
     for r0 in range(0, wl.layer.m, step):
@@ -138,6 +150,7 @@ def test_linear_every_row(wl):
 
 def test_gemm_every_tile(wl):
     _say(wl, "gemm: accumulator at every 128-band, y at those rows per tile")
+    wl.weights().activations()
     m, n = wl.layer.m, wl.layer.n
     rows, cols = band_samples(m), band_samples(n, salt=53)
     rows_t, cols_t = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)

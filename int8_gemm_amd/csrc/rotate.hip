@@ -163,7 +163,6 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   constexpr int NGL = G >= CH ? 1 : CH / G;  // groups held by one lane
   constexpr int KS = LOGG / 2;               // 1/sqrt(g) = 2^-KS
   __shared__ uint32_t s_rowmax[3][256];
-  __shared__ uint32_t s_rowflag[3][256];
   // open elements of wide groups (bf16 only): per row, 1 + the bits of the
   // largest candidate magnitude, and a flag set when an open element's two
   // candidates quantize differently (read one batch later); per thread, the
@@ -181,7 +180,6 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       s_rowmax[q][tid] = 0u;
-      s_rowflag[q][tid] = 0u;
       if constexpr (!F16) {
         s_rowunc[q][tid] = 0u;
         s_rowconf[q][tid] = 0u;
@@ -233,8 +231,6 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   for (; batch < nbatches; ++it, batch += gridDim.x) {
     const int64_t row = batch * rows_per_block + r_in;
     const bool active = in_team && row < rows;
-    uint32_t wn[32];
-    load(batch + gridDim.x, wn);
 
     // ---- exponent span per group (half groups are always exact) ----
     // wide_mask bit gidx: group gidx of this lane spans more binades than the
@@ -337,19 +333,22 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       }
     }
 
+    // the next batch's words, in flight during the rest of this batch (the
+    // transform's float64 registers are free by now)
+    uint32_t wn[32];
+    load(batch + gridDim.x, wn);
     const int slot = it % 3;
     if (active) {
       atomicMax(&s_rowmax[slot][r_in], __float_as_uint(amax));
-      if (unsafe) atomicOr(&s_rowflag[slot][r_in], 1u);
       if constexpr (!F16) {
-        if (has_open) atomicMax(&s_rowunc[slot][r_in], open_hi + 1u);
+        // an unsafe element defers the row: all ones fails every comparison below
+        if (has_open || unsafe) atomicMax(&s_rowunc[slot][r_in], unsafe ? ~0u : open_hi + 1u);
       }
     }
     __syncthreads();
     if (tid < rows_per_block) {
       const int nslot = (it + 2) % 3;
       s_rowmax[nslot][tid] = 0u;
-      s_rowflag[nslot][tid] = 0u;
       if constexpr (!F16) {
         s_rowunc[nslot][tid] = 0u;
         s_rowconf[(it + 1) % 3][tid] = 0u;  // read one batch ago, written next batch
@@ -367,8 +366,7 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     if (active) {
       const float amax_u = __uint_as_float(s_rowmax[slot][r_in]);
       const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact unless deferred
-      bool deferred = s_rowflag[slot][r_in] != 0u || !(amax_u <= 3.0e38f) ||
-                      (amax_u > 0.0f && amax_x < 0x1p-100f);
+      bool deferred = !(amax_u <= 3.0e38f) || (amax_u > 0.0f && amax_x < 0x1p-100f);
       if constexpr (!F16) {
         // an open element's larger candidate reaches the decided absmax
         const uint32_t ru = s_rowunc[slot][r_in];

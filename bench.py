@@ -712,7 +712,7 @@ def _extras(cr, dev, stream, seed, to_dev):
     torch.cuda.synchronize()
 
     # ---- dequant over the 60-layer stack: 60 + 60 distinct int8 buffers of
-    # the two stack shapes, one dequant each per pass, outputs rotated over 4 ----
+    # the two stack shapes and as many outputs, one dequant each per pass ----
     print("[bench] dequant stack", file=sys.stderr, flush=True)
     stack = []
     for lay in (synth.STACK_SQUARE, synth.STACK_WIDE):
@@ -720,22 +720,37 @@ def _extras(cr, dev, stream, seed, to_dev):
         copies = [wq_l.clone() for _ in range(synth.STACK_LAYERS)]
         del wq_l
         outs_l = [torch.empty((lay.n, lay.k), dtype=torch.bfloat16, device=dev)
-                  for _ in range(4)]
+                  for _ in range(synth.STACK_LAYERS)]
         stack.append((copies, sw_l, outs_l))
 
-    def stack_pass(i):
-        for layer_i in range(synth.STACK_LAYERS):
-            for copies, sw_l, outs_l in stack:
-                cr.convrot_dequant_derotate(copies[layer_i], sw_l, g, seed,
-                                            out=outs_l[layer_i % 4])
+    order = [(layer_i, si) for layer_i in range(synth.STACK_LAYERS) for si in range(2)]
+    b_wqs = [stack[si][0][layer_i] for layer_i, si in order]
+    b_sws = [stack[si][1] for layer_i, si in order]
+    b_outs = [stack[si][2][layer_i] for layer_i, si in order]
+
+    def stack_pass(i):  # one batched call: the 120 weights in launches of 48
+        cr.convrot_dequant_derotate_batched(b_wqs, b_sws, g, seed, outs=b_outs)
+
+    def stack_pass_per_layer(i):  # one call per weight
+        for layer_i, si in order:
+            cr.convrot_dequant_derotate(stack[si][0][layer_i], stack[si][1], g, seed,
+                                        out=stack[si][2][layer_i])
 
     stack_ms = _events_time(stack_pass, 3, stream)
+    per_layer_ms = _events_time(stack_pass_per_layer, 3, stream)
     stack_bytes = float(sum(3 * c[0].numel() * len(c) + 4 * len(c) for c, _, _ in stack))
     out["dequant_stack"] = {
-        "layers": 2 * synth.STACK_LAYERS,
+        "layers": 2 * synth.STACK_LAYERS, "call": "convrot_dequant_derotate_batched",
         "GB/s": round(stack_bytes / (stack_ms * 1e-3) / 1e9, 1),
         "frac_hbm": round(stack_bytes / (stack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "ms_per_pass": round(stack_ms, 4), "bytes": stack_bytes}
+        "ms_per_pass": round(stack_ms, 4), "bytes": stack_bytes,
+        "per_layer_calls_ms_per_pass": round(per_layer_ms, 4),
+        "per_layer_calls_frac_hbm": round(stack_bytes / (per_layer_ms * 1e-3) / 1e9
+                                          / PEAK_HBM_GBS, 4)}
+    del b_outs
+    for _, _, outs_l in stack:
+        outs_l.clear()
+    torch.cuda.empty_cache()
 
     # ---- the same stack streamed from pinned host memory: 4608 tokens
     # through every layer, each layer's int8 weight copied to the GPU on the

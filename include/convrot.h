@@ -138,6 +138,34 @@ convrot_status convrot_dequant_derotate_per_channel(const int8_t* wq, const floa
                                                     int64_t k, int g, uint64_t rot_seed,
                                                     uint16_t* w_out, void* stream);
 
+/* Dequantize + derotate several weights in one launch (the default path
+ * decodes every weight of a model on each forward: PR "share the
+ * int8_convrot scheme ... Krea-2 and Z-Image", "What it is worth"; one launch
+ * for many layers spares each small layer the fixed cost of its own launch).
+ * Each job is convrot_dequant_derotate_ex on its own weight; all jobs share
+ * g, rot_seed, scale_mode and out_dtype:
+ *   wq    [n, k] int8 (in, device, 16-byte aligned)
+ *   s_w   [1] or, per channel, [n] fp32 (in, device; 16-byte aligned per channel)
+ *   w_out [n, k] in out_dtype (out, device, 16-byte aligned)
+ * `jobs` is an array of njobs descriptors in HOST memory, read during the
+ * call only: the library copies them into the kernel arguments (up to 48
+ * weights per launch; longer lists take several launches, in order). The
+ * call allocates nothing and reads no device memory on the host, so it can be
+ * captured in a graph. Errors as for the single call, per job; an output that
+ * overlaps another job's output or any job's inputs is CONVROT_E_INVALID_ARG
+ * (inputs may be shared). njobs == 0 is a no-op. Each W_hat is bit-identical
+ * to the single call's. */
+typedef struct convrot_dequant_job {
+  const int8_t* wq;
+  const float* s_w;
+  void* w_out;
+  int64_t n, k;
+} convrot_dequant_job;
+convrot_status convrot_dequant_derotate_batched(const convrot_dequant_job* jobs, int njobs,
+                                                convrot_scale_mode scale_mode, int g,
+                                                uint64_t rot_seed, convrot_dtype out_dtype,
+                                                void* stream);
+
 /* Rotate each token row of x by blockdiag(R), take its absmax and quantize it to
  * int8 with one fp32 scale per row (Invoke docs "int8 Compute", introduction).
  *   x   [m, k] bf16 (in)

@@ -29,6 +29,7 @@ __all__ = [
     "convrot_session_destroy", "convrot_session_linear_int8", "convrot_session_lookup",
     "Session", "EXPORTED_SYMBOLS", "convrot_compute_units", "convrot_set_compute_units",
     "convrot_plan_launch", "KERNELS", "convrot_linear_int8_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "convrot_dequant_derotate_batched",
 ]
 
 ROT_SEED = 0xC0FFEE
@@ -52,6 +53,7 @@ EXPORTED_SYMBOLS = (
     "convrot_streamer_linear_int8", "convrot_session_create", "convrot_session_destroy",
     "convrot_session_linear_int8", "convrot_session_lookup", "convrot_compute_units",
     "convrot_set_compute_units", "convrot_plan_launch", "convrot_linear_int8_noalloc",
+    "convrot_dequant_derotate_batched",
 )
 
 # bytes of the per-device scratch array behind convrot_linear_int8_noalloc
@@ -59,6 +61,11 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # convrot_kernel values (convrot_plan_launch)
 KERNELS = {"act_quant": 0, "act_quant_deferred": 1, "exact": 2, "dequant": 3, "gemm": 4}
+
+
+class _DequantJob(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class _LaunchPlan(ctypes.Structure):
@@ -132,6 +139,7 @@ def load_library():
                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)],
             "convrot_set_compute_units": [I],
             "convrot_linear_int8_noalloc": [P, P, P, I, P, I64, I64, I64, I, U64, P, I, P],
+            "convrot_dequant_derotate_batched": [ctypes.POINTER(_DequantJob), I, I, I, U64, I, P],
             "convrot_plan_launch": [I, I64, I64, I64, I, I, ctypes.POINTER(_LaunchPlan)],
         }
         for name, args in sig.items():
@@ -685,3 +693,37 @@ def convrot_linear_int8_noalloc(x: torch.Tensor, wq: torch.Tensor, s_w: torch.Te
                                                       _ptr(bias), m, n, k, g, rot_seed,
                                                       _ptr(out), dt, _stream(x)))
     return out
+
+
+def convrot_dequant_derotate_batched(wqs, s_ws, g: int, rot_seed: int = ROT_SEED, *,
+                                     per_channel: bool = False,
+                                     out_dtype: torch.dtype = torch.bfloat16, outs=None):
+    """W_hat of every (wq, s_w) pair in one batched call (launches of up to 48
+    weights): the list of each weight's int8 [n, k] and scale; returns the
+    list of outputs [n, k] in out_dtype (or fills `outs`)."""
+    if len(wqs) != len(s_ws):
+        raise ValueError("one scale per weight")
+    if outs is None:
+        outs = [torch.empty(w.shape, dtype=out_dtype, device=w.device) for w in wqs]
+    if len(outs) != len(wqs):
+        raise ValueError("one output per weight")
+    jobs = (_DequantJob * max(len(wqs), 1))()
+    dt = None
+    for i, (wq, s_w, out) in enumerate(zip(wqs, s_ws, outs)):
+        _need(wq, "wq", torch.int8, 2)
+        n, k = wq.shape
+        _need_sw(s_w, per_channel, n)
+        d = _need16(out, "out", 2)
+        if dt is not None and d != dt:
+            raise TypeError("every output has the same format")
+        dt = d
+        if tuple(out.shape) != (n, k):
+            raise ValueError(f"output {i} has shape {tuple(out.shape)}, want {(n, k)}")
+        _same_device(wq, s_w, out, wqs[0])
+        jobs[i] = _DequantJob(wq.data_ptr(), s_w.data_ptr(), out.data_ptr(), n, k)
+    if not wqs:
+        return outs
+    mode = _SCALE_PER_CHANNEL if per_channel else _SCALE_PER_TENSOR
+    _check(load_library().convrot_dequant_derotate_batched(jobs, len(wqs), mode, g, rot_seed, dt,
+                                                           _stream(wqs[0])))
+    return outs

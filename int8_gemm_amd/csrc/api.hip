@@ -307,6 +307,48 @@ convrot_status convrot_dequant_derotate_ex(const int8_t* wq, const float* s_w,
                       stream);
 }
 
+convrot_status convrot_dequant_derotate_batched(const convrot_dequant_job* jobs, int njobs,
+                                                convrot_scale_mode scale_mode, int g,
+                                                uint64_t rot_seed, convrot_dtype out_dtype,
+                                                void* stream) {
+  const char* fn = "convrot_dequant_derotate_batched";
+  bool pc;
+  DType dt;
+  if (!scale_mode_of(scale_mode, &pc) || !dtype_of(out_dtype, &dt))
+    return fail(CONVROT_E_INVALID_ARG, "%s: scale_mode=%d out_dtype=%d", fn, (int)scale_mode,
+                (int)out_dtype);
+  if (njobs < 0 || (njobs > 0 && !jobs))
+    return fail(CONVROT_E_INVALID_ARG, "%s: njobs=%d, jobs=%p", fn, njobs, (const void*)jobs);
+  if (!valid_group(g)) return fail(CONVROT_E_UNSUPPORTED_GROUP, "%s: g=%d", fn, g);
+  std::vector<DequantJob> js((size_t)njobs);
+  for (int i = 0; i < njobs; ++i) {
+    const convrot_dequant_job& jb = jobs[i];
+    if (!jb.wq || !jb.s_w || !jb.w_out)
+      return fail(CONVROT_E_INVALID_ARG, "%s: job %d: null pointer", fn, i);
+    if (jb.n <= 0) return fail(CONVROT_E_INVALID_ARG, "%s: job %d: n=%lld", fn, i, (long long)jb.n);
+    if (convrot_status st = check_rot(fn, jb.n, jb.k, g)) return st;
+    if (!aligned(jb.wq, 16) || !aligned(jb.w_out, 16) || !sw_aligned(pc, jb.s_w))
+      return fail(CONVROT_E_MISALIGNED, "%s: job %d: misaligned pointer", fn, i);
+    js[(size_t)i] = DequantJob{jb.wq, jb.s_w, static_cast<uint16_t*>(jb.w_out), jb.n, jb.k};
+  }
+  // every output is written by its job alone and read by none
+  for (int i = 0; i < njobs; ++i) {
+    const size_t ob = (size_t)(js[i].n * js[i].k) * 2;
+    for (int j = 0; j < njobs; ++j) {
+      const size_t nb = (size_t)(js[j].n * js[j].k);
+      if (overlap(js[i].w_out, ob, js[j].wq, nb) ||
+          overlap(js[i].w_out, ob, js[j].s_w, sw_bytes(pc, js[j].n)) ||
+          (j != i && overlap(js[i].w_out, ob, js[j].w_out, nb * 2)))
+        return fail(CONVROT_E_INVALID_ARG, "%s: job %d's output overlaps job %d's buffers", fn,
+                    i, j);
+    }
+  }
+  if (njobs == 0) return ok();
+  const SignMask sm = make_signs(rot_seed, g);
+  return hip_status(launch_dequant_jobs(js.data(), njobs, pc, g, sm, dt, (hipStream_t)stream),
+                    fn);
+}
+
 static convrot_status quantize_activations_impl(const char* fn, bool exact, DType dt,
                                                 const uint16_t* x, int64_t m, int64_t k, int g,
                                                 uint64_t rot_seed, int8_t* xq, float* s_x,

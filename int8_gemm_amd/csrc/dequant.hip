@@ -56,19 +56,16 @@ __device__ __forceinline__ v4i frag_from_masks(uint32_t neg, uint32_t nz) {
   return f;
 }
 
-template <int G, bool PC, bool F16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1))) void dequant_kernel(const int8_t* __restrict__ wq,
-                                                      const float* __restrict__ s_w,
-                                                      int64_t nrows, int vrows_per_ch,
-                                                      double inv_vrows_per_ch, SignMask sm,
-                                                      uint16_t* __restrict__ out) {
+template <int G, bool PC, bool F16, int NJ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1))) void dequant_kernel(
+    const DequantJobs<NJ> jobs, SignMask sm) {
   constexpr int R = G > 32 ? G : 32;   // bytes per view row
   constexpr int NB = R / 32;           // 32-blocks per view row
   constexpr int KS = ilog2(G) / 2;
   // A block takes 4 tiles of 32 view rows, or one tile whose 8 output
   // 32-blocks are spread over its 4 waves (g = 256): a contiguous chunk of
-  // CHUNK input bytes, loaded coalesced into LDS and prefetched one chunk
-  // ahead through registers.
+  // CHUNK input bytes of one weight, loaded coalesced into LDS and
+  // prefetched one chunk ahead through registers.
   constexpr int NQ = NB >= 4 ? 4 : 1;      // waves per tile
   constexpr int JW = NB / NQ;              // output 32-blocks per wave
   constexpr int TPB = 4 / NQ;              // tiles per block
@@ -116,20 +113,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1)
     fragN[0] = fragP[0];
   }
 
-  const float c_t = PC ? 0.0f : *s_w * (1.0f / (float)(1 << KS));
-  const int64_t ntiles = (nrows + 31) / 32;
-  const int64_t nchunks = (ntiles + TPB - 1) / TPB;
-  const int64_t in_bytes = nrows * R;
+  // The chunks of all weights form one sequence (weight j owns chunks
+  // [chunk_begin[j], chunk_begin[j + 1])); a block walks chunks blockIdx.x,
+  // blockIdx.x + gridDim.x, ... The fields of the weight of the current and
+  // of the next chunk stay in registers and are read again only when the
+  // weight changes (chunks only grow).
+  const int64_t nchunks = jobs.chunk_begin[NJ == 1 ? 1 : jobs.njobs];
+  struct Cur {
+    int j;
+    int64_t begin, end;  // its chunks
+    const int8_t* wq;
+    uint16_t* out;
+    int64_t nrows;
+    float ct;  // per tensor: RN(s_w * 2^-KS)
+  };
+  auto fetch = [&](int64_t ch, int j) {
+    while (NJ > 1 && j + 1 < jobs.njobs && ch >= jobs.chunk_begin[j + 1]) ++j;
+    Cur c;
+    c.j = j;
+    c.begin = NJ == 1 ? 0 : jobs.chunk_begin[j];  // a table of one starts at chunk 0
+    c.end = jobs.chunk_begin[j + 1];
+    c.wq = jobs.job[j].wq;
+    c.out = jobs.job[j].w_out;
+    c.nrows = jobs.job[j].nrows;
+    c.ct = PC ? 0.0f : *jobs.job[j].s_w * (1.0f / (float)(1 << KS));
+    return c;
+  };
 
   // coalesced chunk load: thread tid takes 16-byte pieces tid, tid + 256, ...
-  // (bytes past the end read as zero)
-  auto load_chunk = [&](int64_t ch, u4 (&r)[NLD > 0 ? NLD : 1]) {
+  // (bytes past the weight's end read as zero)
+  auto load_chunk = [&](int64_t ch, const Cur& w, u4 (&r)[NLD > 0 ? NLD : 1]) {
+    const int64_t in_bytes = w.nrows * R;
+    const int64_t base = (ch - w.begin) * CHUNK;
 #pragma unroll
     for (int i = 0; i < (NLD > 0 ? NLD : 1); ++i) {
       const int off = (tid + 256 * i) * 16;
-      const int64_t g = ch * CHUNK + off;
+      const int64_t g = base + off;
       r[i] = (ch < nchunks && off < CHUNK && g < in_bytes)
-                 ? *reinterpret_cast<const u4*>(wq + g)
+                 ? *reinterpret_cast<const u4*>(w.wq + g)
                  : (u4){0u, 0u, 0u, 0u};
     }
   };
@@ -143,22 +164,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1)
 
   u4 pre[NLD > 0 ? NLD : 1];
   int64_t ch = blockIdx.x;
-  load_chunk(ch, pre);
+  Cur cur = fetch(ch, 0);
+  load_chunk(ch, cur, pre);
   store_chunk(pre);
   __syncthreads();
   for (; ch < nchunks; ch += gridDim.x) {
-    load_chunk(ch + gridDim.x, pre);  // next chunk, in flight during this one
+    const int64_t chn = ch + gridDim.x;
+    const Cur nxt = (NJ > 1 && chn >= cur.end && chn < nchunks) ? fetch(chn, cur.j) : cur;
+    load_chunk(chn, nxt, pre);  // next chunk, in flight during this one
 
-    const int64_t tile = ch * TPB + tl;
-    float c = c_t;
+    const int64_t nrows = cur.nrows;
+    uint16_t* __restrict__ out = cur.out;
+    const int64_t tile = (ch - cur.begin) * TPB + tl;
+    float c;
     if constexpr (PC) {
       // weight row of view row vr: q = vr / vrows_per_ch from a float64
       // estimate (vr < 2^53), corrected by one either way
+      const int vpc = jobs.job[cur.j].vrows_per_ch;
       const int64_t vr = tile * 32 + jl < nrows ? tile * 32 + jl : nrows - 1;
-      int64_t q = (int64_t)((double)vr * inv_vrows_per_ch);
-      if (q * vrows_per_ch > vr) --q;
-      if ((q + 1) * vrows_per_ch <= vr) ++q;
-      c = s_w[q] * (1.0f / (float)(1 << KS));
+      int64_t q = (int64_t)((double)vr * jobs.job[cur.j].inv_vrows_per_ch);
+      if (q * vpc > vr) --q;
+      if ((q + 1) * vpc <= vr) ++q;
+      c = jobs.job[cur.j].s_w[q] * (1.0f / (float)(1 << KS));
+    } else {
+      c = cur.ct;
     }
     v4i bfr[NB];
 #pragma unroll
@@ -205,54 +234,99 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PC ? 4 : 1)
     __syncthreads();  // every wave is done with s_in and its own s_out
     store_chunk(pre);
     __syncthreads();
+    cur = nxt;
   }
 }
 
 }  // namespace
 
-template <int G>
-static void launch_g(bool pc, bool f16, int64_t blocks, const int8_t* wq, const float* s_w,
-                     int64_t nrows, int vrows_per_ch, const SignMask& sm, uint16_t* w_out,
-                     hipStream_t st) {
-  auto kern = f16 ? (pc ? dequant_kernel<G, true, true> : dequant_kernel<G, false, true>)
-                  : (pc ? dequant_kernel<G, true, false> : dequant_kernel<G, false, false>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, wq, s_w, nrows,
-                     vrows_per_ch, 1.0 / (double)vrows_per_ch, sm, w_out);
+template <int G, int NJ>
+static void launch_g(bool pc, bool f16, int64_t blocks, const DequantJobs<NJ>& jobs,
+                     const SignMask& sm, hipStream_t st) {
+  auto kern = f16 ? (pc ? dequant_kernel<G, true, true, NJ> : dequant_kernel<G, false, true, NJ>)
+                  : (pc ? dequant_kernel<G, true, false, NJ> : dequant_kernel<G, false, false, NJ>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, jobs, sm);
+}
+
+// 32-row tiles per block step: one at g = 256 (its 8 output blocks spread
+// over the 4 waves), four at g <= 64.
+static int tiles_per_step(int g) { return (g > 32 ? g : 32) / 32 >= 4 ? 1 : 4; }
+
+static int64_t dequant_chunks(int64_t n, int64_t k, int g) {
+  const int R = g > 32 ? g : 32;
+  const int64_t tiles = (n * k / R + 31) / 32;
+  const int tpb = tiles_per_step(g);
+  return (tiles + tpb - 1) / tpb;
 }
 
 // Persistent blocks per CU, as measured: 2 when a block step is one tile
 // (g = 256; 4 blocks were 4-18% slower on 3072x3072 .. 13824x5120), 4 when
 // it is four (g <= 64, where 2 or 3 were up to 11% slower).
-LaunchPlan plan_dequant(int64_t n, int64_t k, int g, int cus) {
+static LaunchPlan plan_chunks(int64_t chunks, int g, int cus) {
   LaunchPlan p;
   p.block = 256;
-  const int R = g > 32 ? g : 32;
-  const int64_t nrows = n * k / R;
-  const int64_t tiles = (nrows + 31) / 32;
-  p.rows_per_block = (R / 32 >= 4) ? 1 : 4;  // 32-row tiles per block step
-  const int64_t chunks = (tiles + p.rows_per_block - 1) / p.rows_per_block;
+  p.rows_per_block = tiles_per_step(g);
   const int64_t cap = (int64_t)(cus > 0 ? cus : 1) * (p.rows_per_block == 1 ? 2 : 4);
   p.grid = chunks < cap ? chunks : cap;
   p.passes = p.grid > 0 ? (chunks + p.grid - 1) / p.grid : 0;
   return p;
 }
 
+LaunchPlan plan_dequant(int64_t n, int64_t k, int g, int cus) {
+  return plan_chunks(dequant_chunks(n, k, g), g, cus);
+}
+
+// Launches of up to NJ weights each (NJ = 1 for a single weight).
+template <int NJ>
+static hipError_t launch_jobs(const DequantJob* job, int njobs, bool sw_per_channel, int g,
+                              const SignMask& sm, DType dt, hipStream_t st) {
+  const int R = g > 32 ? g : 32;
+  const int cus = compute_units();
+  for (int j0 = 0; j0 < njobs;) {
+    DequantJobs<NJ> jobs;
+    jobs.njobs = 0;
+    int64_t chunks = 0;
+    for (; j0 < njobs && jobs.njobs < NJ; ++j0) {
+      const int64_t c = dequant_chunks(job[j0].n, job[j0].k, g);
+      if (c == 0) continue;  // an empty weight has nothing to decode
+      typename DequantJobs<NJ>::Desc& d = jobs.job[jobs.njobs];
+      d.wq = job[j0].wq;
+      d.s_w = job[j0].s_w;
+      d.w_out = job[j0].w_out;
+      d.nrows = job[j0].n * job[j0].k / R;
+      d.vrows_per_ch = (int)(job[j0].k / R);  // K % R == 0 for every supported (K, g)
+      d.inv_vrows_per_ch = 1.0 / (double)d.vrows_per_ch;
+      jobs.chunk_begin[jobs.njobs] = chunks;
+      chunks += c;
+      ++jobs.njobs;
+    }
+    if (jobs.njobs == 0) continue;
+    jobs.chunk_begin[jobs.njobs] = chunks;
+    const int64_t blocks = plan_chunks(chunks, g, cus).grid;
+    const bool pc = sw_per_channel, f16 = dt == DType::kF16;
+    switch (g) {
+      case 4: launch_g<4, NJ>(pc, f16, blocks, jobs, sm, st); break;
+      case 16: launch_g<16, NJ>(pc, f16, blocks, jobs, sm, st); break;
+      case 64: launch_g<64, NJ>(pc, f16, blocks, jobs, sm, st); break;
+      default: launch_g<256, NJ>(pc, f16, blocks, jobs, sm, st); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dequant_jobs(const DequantJob* job, int njobs, bool sw_per_channel, int g,
+                               const SignMask& sm, DType dt, hipStream_t st) {
+  return njobs == 1 ? launch_jobs<1>(job, njobs, sw_per_channel, g, sm, dt, st)
+                    : launch_jobs<kMaxDequantJobs>(job, njobs, sw_per_channel, g, sm, dt, st);
+}
+
 hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,
                           int64_t k, int g, const SignMask& sm, uint16_t* w_out, DType dt,
                           hipStream_t st) {
-  if (n * k == 0) return hipSuccess;
-  const LaunchPlan p = plan_dequant(n, k, g, compute_units());
-  const int R = g > 32 ? g : 32;
-  const int64_t nrows = n * k / R;
-  const int vrows_per_ch = (int)(k / R);  // K % R == 0 for every supported (K, g)
-  const bool pc = sw_per_channel, f16 = dt == DType::kF16;
-  switch (g) {
-    case 4: launch_g<4>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 16: launch_g<16>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    case 64: launch_g<64>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-    default: launch_g<256>(pc, f16, p.grid, wq, s_w, nrows, vrows_per_ch, sm, w_out, st); break;
-  }
-  return hipGetLastError();
+  const DequantJob job{wq, s_w, w_out, n, k};
+  return launch_dequant_jobs(&job, 1, sw_per_channel, g, sm, dt, st);
 }
 
 }  // namespace convrot

@@ -41,6 +41,35 @@ hipError_t launch_quantize_rows_exact(const uint16_t* x, int8_t* xq, float* s, i
 // absmax accumulator until the last launch).
 hipError_t launch_quantize_tensor(const uint16_t* w, int8_t* wq, float* s_w, int64_t rows, int K,
                                   int g, const SignMask& sm, hipStream_t st);
+// One weight of a batched dequant.
+struct DequantJob {
+  const int8_t* wq;
+  const float* s_w;
+  uint16_t* w_out;
+  int64_t n, k;
+};
+// The weights of one dequant launch, passed by value as kernel arguments
+// (a single weight gets a table of one: the argument block stays small, and
+// with it the launch).
+constexpr int kMaxDequantJobs = 48;
+template <int N>
+struct DequantJobs {
+  struct Desc {
+    const int8_t* wq;
+    const float* s_w;
+    uint16_t* w_out;
+    int64_t nrows;            // view rows of max(g, 32) bytes
+    double inv_vrows_per_ch;  // per-channel: 1 / view rows per weight row
+    int vrows_per_ch;
+  };
+  int njobs;
+  int64_t chunk_begin[N + 1];
+  Desc job[N];
+};
+// W_hat of several weights that share g, the signs, the scale mode and the
+// output format, in launches of up to kMaxDequantJobs weights each.
+hipError_t launch_dequant_jobs(const DequantJob* job, int njobs, bool sw_per_channel, int g,
+                               const SignMask& sm, DType dt, hipStream_t st);
 // W_hat = RN16(float(S) * RN(s_w * 2^-log2(sqrt g))), S = (Wq . D) . H per
 // group, RN16 to bf16 or half (dt); with sw_per_channel, row r uses s_w[r].
 hipError_t launch_dequant(const int8_t* wq, const float* s_w, bool sw_per_channel, int64_t n,

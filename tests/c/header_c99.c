@@ -60,6 +60,16 @@ int convrot_header_c99_check(void* p, int i) {
       s = convrot_linear_int8_noalloc(p, q, f, CONVROT_SCALE_PER_TENSOR, p, 1, 16, 64, 4, 1u, p,
                                       CONVROT_DTYPE_BF16, p);
     }
+    {
+      convrot_dequant_job job;
+      job.wq = q;
+      job.s_w = f;
+      job.w_out = p;
+      job.n = 1;
+      job.k = 64;
+      s = convrot_dequant_derotate_batched(&job, 1, CONVROT_SCALE_PER_TENSOR, 4, 1u,
+                                           CONVROT_DTYPE_BF16, p);
+    }
   }
   return (int)s + convrot_abi_version() + (int)CONVROT_ABI_VERSION + tile + latched + (int)err;
 }

@@ -341,3 +341,26 @@ def test_noalloc_argument_checks_without_gpu(lib):
     assert fn(P, P, P, 0, None, 8, 16, 64, 4, 1, P, 9, None) == 1
     assert fn(P, P, P, 0, None, 0, 16, 64, 4, 1, P, 0, None) == 0
     assert cr.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_batched_dequant_argument_checks_without_gpu(lib):
+    """Every job is checked before anything is launched; outputs may not
+    overlap another job's buffers, inputs may be shared; no jobs is a no-op."""
+    J = cr._DequantJob
+    fn = lib.convrot_dequant_derotate_batched
+
+    def call(*jobs, g=256, mode=0, dt=0):
+        arr = (J * max(len(jobs), 1))(*jobs)
+        return fn(arr, len(jobs), mode, g, 1, dt, None)
+
+    a, b, c, d = (1 << 24), (1 << 26), (1 << 28), (1 << 30)
+    assert fn(None, 0, 0, 256, 1, 0, None) == 0
+    assert fn(None, 2, 0, 256, 1, 0, None) == 1                     # null list
+    assert call(J(a, b, c, 16, 256), g=3) == 2                      # group
+    assert call(J(a, b, c, 16, 320)) == 2                           # k % g
+    assert call(J(a, b, c, 16, 256), J(a, b, c + 4, 16, 256)) == 4  # misaligned output
+    assert call(J(a, b, c, 16, 256), J(a, b, c + 4096, 16, 256)) == 1  # outputs overlap
+    assert call(J(a, b, c, 16, 256), J(c, b, d, 16, 256)) == 1      # output is an input
+    assert call(J(a, b, c, 16, 256), J(0, b, d, 16, 256)) == 1      # null weight
+    assert call(J(a, b, c, 16, 256), mode=5) == 1                   # unknown enum
+    assert lib.convrot_last_error_string()

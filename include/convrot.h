@@ -330,12 +330,13 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const vo
  * for a key, synchronously on `stream`:
  *   1. the first token slice is quantized and every GEMM tile that exists
  *      for k is timed on it (two runs each, after 256 MB - the MI355X MALL -
- *      have been written to a temporary buffer); the fastest is kept;
+ *      have been written to the session's buffer); the fastest is kept;
  *   2. the forward runs with that tile and writes y;
- *   3. W_hat (convrot_dequant_derotate_ex in dtype) is formed in a temporary
- *      buffer, the first min(m, 256) rows of x . W_hat^T (+ bias) are computed
- *      in fp32, and their relative Frobenius distance e from the same rows of
- *      y is kept. e <= check_tolerance passes.
+ *   3. W_hat (convrot_dequant_derotate_ex in dtype) is formed in the
+ *      session's buffer, a chunk of weight rows at a time, the first
+ *      min(m, 256) rows of x . W_hat^T (+ bias) are computed in fp32 over the
+ *      chunk's columns, and their relative Frobenius distance e from the same
+ *      rows of y (summed over all chunks) is kept. e <= check_tolerance passes.
  * Later calls for the key run the forward with the kept tile and enqueue
  * asynchronously, like convrot_linear_int8_ex (same results: every tile gives
  * the same bits). If the check fails, or a HIP call of a first call fails,
@@ -344,9 +345,10 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const vo
  * default path (convrot_dequant_derotate_ex and its own bf16 / fp16 matmul).
  * The library never switches paths silently. The quantization noise of the
  * int8 path is a few percent at most (per-token int8 after the rotation);
- * check_tolerance <= 0 selects 0.1. First calls allocate and free temporary
- * device memory (256 MB + 2nk + 1 KB per row of n outputs). A session is
- * safe to share between threads (calls are serialized). */
+ * check_tolerance <= 0 selects 0.1. convrot_session_create allocates the
+ * session's buffer (256 MB of device memory) and two events on the current
+ * device; convrot_session_destroy frees them. The calls allocate no device
+ * memory. A session is safe to share between threads (calls are serialized). */
 typedef struct convrot_session convrot_session;
 convrot_status convrot_session_create(double check_tolerance, convrot_session** out);
 convrot_status convrot_session_destroy(convrot_session* session);

@@ -786,8 +786,11 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* s, const void* x, 
 
 namespace {
 
-constexpr size_t kFlushBytes = (size_t)256 << 20;  // MI355X MALL
+// One device buffer per session: written whole before each timed tile run
+// (256 MB, the MI355X MALL), then reused for the check.
+constexpr size_t kSessionScratch = (size_t)256 << 20;
 constexpr int kCheckRows = 256;
+constexpr size_t kPartialBytes = (size_t)kCheckRows * 2 * sizeof(double);
 
 struct SessionEntry {
   int tile;
@@ -802,14 +805,14 @@ int token_bucket(int64_t m) {
   return b;  // ceil(log2 m)
 }
 
-// device buffers freed on scope exit
-struct DeviceTemp {
-  void* p = nullptr;
-  hipError_t alloc(size_t bytes) { return hipMalloc(&p, bytes); }
-  ~DeviceTemp() {
-    if (p) (void)hipFree(p);
-  }
-};
+// Weight rows per check chunk: partial sums, y_ref [kCheckRows, nc] fp32 and
+// W_hat [nc, k] in 16-bit must fit the session buffer; a multiple of 64
+// (k <= 16384 gives nc >= 7936).
+int64_t check_chunk_rows(int64_t n, int64_t k) {
+  int64_t nc = (int64_t)((kSessionScratch - kPartialBytes - 256) /
+                         (size_t)(2 * k + 4 * kCheckRows)) / 64 * 64;
+  return nc < n ? nc : n;
+}
 
 }  // namespace
 
@@ -820,6 +823,14 @@ struct convrot_session {
   std::string latch_reason;
   std::map<SessionKey, SessionEntry> entries;
   std::mutex mu;
+  void* scratch = nullptr;  // kSessionScratch bytes on `device`
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  double host[2 * kCheckRows];
+  ~convrot_session() {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (scratch) (void)hipFree(scratch);
+  }
 };
 
 convrot_status convrot_session_create(double check_tolerance, convrot_session** out) {
@@ -830,7 +841,10 @@ convrot_status convrot_session_create(double check_tolerance, convrot_session** 
     return fail(CONVROT_E_INVALID_ARG, "%s: tolerance is NaN", fn);
   convrot_session* s = new convrot_session();
   s->tol = check_tolerance > 0 ? check_tolerance : 0.1;
-  const hipError_t e = hipGetDevice(&s->device);
+  hipError_t e = hipGetDevice(&s->device);
+  if (e == hipSuccess) e = hipMalloc(&s->scratch, kSessionScratch);
+  if (e == hipSuccess) e = hipEventCreate(&s->e0);
+  if (e == hipSuccess) e = hipEventCreate(&s->e1);
   if (e != hipSuccess) {
     delete s;
     return hip_status(e, fn);
@@ -845,8 +859,9 @@ convrot_status convrot_session_destroy(convrot_session* s) {
   return ok();
 }
 
-// The first call for a key: tune, run, check. Returns the status; on success
-// *entry holds the kept tile and the check's error.
+// The first call for a key: tune, run, check, in the session's buffer and
+// events (nothing allocated). Returns the status; on success *entry holds the
+// kept tile and the check's error.
 static convrot_status session_first_call(const char* fn, convrot_session* s, bool pc, DType dt,
                                          const uint16_t* x, const int8_t* wq, const float* s_w,
                                          const uint16_t* bias, int64_t m, int64_t n, int64_t k,
@@ -861,60 +876,55 @@ static convrot_status session_first_call(const char* fn, convrot_session* s, boo
   // 1. time every tile that exists for k on the first slice, caches flushed
   int best = 0;
   float best_ms = 0.0f;
-  {
-    DeviceTemp flush;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (e == hipSuccess) e = flush.alloc(kFlushBytes);
-    if (e == hipSuccess) e = hipEventCreate(&e0);
-    if (e == hipSuccess) e = hipEventCreate(&e1);
-    const int cands[] = {384, 256, 192, 128};
-    for (int c : cands) {
-      if (e != hipSuccess) break;
-      if (c == 384 && k % 128 != 0) continue;
-      for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
-        e = launch_flush(flush.p, kFlushBytes, st);
-        if (e == hipSuccess) e = hipEventRecord(e0, st);
-        if (e == hipSuccess)
-          e = launch_gemm_tile(xq, sx, wq, s_w, pc, bias, rows0, n, k, y, nullptr, c, dt, st);
-        if (e == hipSuccess) e = hipEventRecord(e1, st);
-        if (e == hipSuccess) e = hipEventSynchronize(e1);
-        float ms = 0.0f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-        if (e == hipSuccess && (best == 0 || ms < best_ms)) {
-          best = c;
-          best_ms = ms;
-        }
+  const int cands[] = {384, 256, 192, 128};
+  for (int c : cands) {
+    if (e != hipSuccess) break;
+    if (c == 384 && k % 128 != 0) continue;
+    for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+      e = launch_flush(s->scratch, kSessionScratch, st);
+      if (e == hipSuccess) e = hipEventRecord(s->e0, st);
+      if (e == hipSuccess)
+        e = launch_gemm_tile(xq, sx, wq, s_w, pc, bias, rows0, n, k, y, nullptr, c, dt, st);
+      if (e == hipSuccess) e = hipEventRecord(s->e1, st);
+      if (e == hipSuccess) e = hipEventSynchronize(s->e1);
+      float ms = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, s->e0, s->e1);
+      if (e == hipSuccess && (best == 0 || ms < best_ms)) {
+        best = c;
+        best_ms = ms;
       }
     }
-    if (e0) (void)hipEventDestroy(e0);
-    if (e1) (void)hipEventDestroy(e1);
   }
   if (e != hipSuccess) return hip_status(e, fn);
   // 2. the forward with the kept tile
   if (convrot_status r = linear_run(fn, pc, dt, x, wq, s_w, bias, m, n, k, g, rot_seed, y,
                                     workspace, slice, st, best))
     return r;
-  // 3. the check against the default path on the first rows
+  // 3. the check against the default path on the first rows, over chunks of
+  // weight rows: W_hat of the chunk, then y_ref of its columns
   const int rows = (int)(m < kCheckRows ? m : kCheckRows);
-  DeviceTemp w_hat, y_ref, partial;
-  e = w_hat.alloc((size_t)(n * k) * 2);
-  if (e == hipSuccess) e = y_ref.alloc((size_t)rows * (size_t)n * 4);
-  if (e == hipSuccess) e = partial.alloc((size_t)rows * 2 * sizeof(double));
+  const int64_t nc = check_chunk_rows(n, k);
+  uint8_t* buf = static_cast<uint8_t*>(s->scratch);
+  double* partial = reinterpret_cast<double*>(buf);
+  float* y_ref = reinterpret_cast<float*>(buf + align_up(kPartialBytes, 256));
+  uint16_t* w_hat = reinterpret_cast<uint16_t*>(
+      buf + align_up(kPartialBytes, 256) + align_up((size_t)kCheckRows * (size_t)nc * 4, 256));
+  for (int64_t n0 = 0; n0 < n && e == hipSuccess; n0 += nc) {
+    const int64_t nn = n - n0 < nc ? n - n0 : nc;
+    e = launch_dequant(wq + n0 * k, pc ? s_w + n0 : s_w, pc, nn, k, g, sm, w_hat, dt, st);
+    if (e == hipSuccess)
+      e = launch_check_rows(x, w_hat, bias ? bias + n0 : nullptr, y + n0, n, rows, (int)nn,
+                            (int)k, dt, n0 > 0, y_ref, partial, st);
+  }
   if (e == hipSuccess)
-    e = launch_dequant(wq, s_w, pc, n, k, g, sm, static_cast<uint16_t*>(w_hat.p), dt, st);
-  if (e == hipSuccess)
-    e = launch_check_rows(x, static_cast<const uint16_t*>(w_hat.p), bias, y, rows, (int)n, (int)k,
-                          dt, static_cast<float*>(y_ref.p), static_cast<double*>(partial.p), st);
-  std::vector<double> host((size_t)rows * 2);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(host.data(), partial.p, host.size() * sizeof(double),
+    e = hipMemcpyAsync(s->host, partial, (size_t)rows * 2 * sizeof(double),
                        hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_status(e, fn);
   double d2 = 0.0, r2 = 0.0;
   for (int r = 0; r < rows; ++r) {
-    d2 += host[2 * r];
-    r2 += host[2 * r + 1];
+    d2 += s->host[2 * r];
+    r2 += s->host[2 * r + 1];
   }
   entry->tile = best;
   entry->err = r2 > 0.0 ? std::sqrt(d2 / r2) : (d2 == 0.0 ? 0.0 : INFINITY);

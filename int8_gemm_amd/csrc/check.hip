@@ -7,7 +7,8 @@
 //   ref_rows_kernel:  y_ref[r, c] = sum_k x[r, k] * W_hat[c, k] (+ bias[c]) in
 //                     fp32, W_hat the dequantized (default-path) weight;
 //   diff_rows_kernel: per row, sum (y[r, c] - y_ref[r, c])^2 and
-//                     sum y_ref[r, c]^2 in float64;
+//                     sum y_ref[r, c]^2 in float64 (added up over the
+//                     column chunks the check is taken in);
 //   flush_kernel:     writes a buffer, evicting the operands from the caches.
 //
 // None of this is on the forward's hot path: it runs once per key.
@@ -71,16 +72,18 @@ __global__ __launch_bounds__(256) void ref_rows_kernel(const uint16_t* __restric
   }
 }
 
-// one block per row
+// one block per row; the sums are added to partial when `accumulate` is set
+// (a check taken over column chunks)
 template <bool F16>
-__global__ __launch_bounds__(256) void diff_rows_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(256) void diff_rows_kernel(const uint16_t* __restrict__ y, int64_t ldy,
                                                         const float* __restrict__ y_ref, int n,
+                                                        int accumulate,
                                                         double* __restrict__ partial) {
   __shared__ double s0[256], s1[256];
   const int row = blockIdx.x, tid = threadIdx.x;
   double d2 = 0.0, r2 = 0.0;
   for (int c = tid; c < n; c += 256) {
-    const double a = to_f32<F16>(y[(int64_t)row * n + c]);
+    const double a = to_f32<F16>(y[(int64_t)row * ldy + c]);
     const double b = y_ref[(int64_t)row * n + c];
     d2 += (a - b) * (a - b);
     r2 += b * b;
@@ -96,8 +99,8 @@ __global__ __launch_bounds__(256) void diff_rows_kernel(const uint16_t* __restri
     __syncthreads();
   }
   if (tid == 0) {
-    partial[2 * row] = s0[0];
-    partial[2 * row + 1] = s1[0];
+    partial[2 * row] = (accumulate ? partial[2 * row] : 0.0) + s0[0];
+    partial[2 * row + 1] = (accumulate ? partial[2 * row + 1] : 0.0) + s1[0];
   }
 }
 
@@ -118,20 +121,21 @@ hipError_t launch_flush(void* buf, size_t bytes, hipStream_t st) {
 }
 
 hipError_t launch_check_rows(const uint16_t* x, const uint16_t* w_hat, const uint16_t* bias,
-                             const uint16_t* y, int rows, int n, int k, DType dt, float* y_ref,
-                             double* partial, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+                             const uint16_t* y, int64_t ldy, int rows, int n, int k, DType dt,
+                             bool accumulate, float* y_ref, double* partial, hipStream_t st) {
+  if (rows <= 0 || n <= 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((rows + 63) / 64));
+  const int acc = accumulate ? 1 : 0;
   if (dt == DType::kF16) {
     hipLaunchKernelGGL(ref_rows_kernel<true>, grid, dim3(256), 0, st, x, w_hat, bias, rows, n, k,
                        y_ref);
-    hipLaunchKernelGGL(diff_rows_kernel<true>, dim3((unsigned)rows), dim3(256), 0, st, y, y_ref,
-                       n, partial);
+    hipLaunchKernelGGL(diff_rows_kernel<true>, dim3((unsigned)rows), dim3(256), 0, st, y, ldy,
+                       y_ref, n, acc, partial);
   } else {
     hipLaunchKernelGGL(ref_rows_kernel<false>, grid, dim3(256), 0, st, x, w_hat, bias, rows, n,
                        k, y_ref);
-    hipLaunchKernelGGL(diff_rows_kernel<false>, dim3((unsigned)rows), dim3(256), 0, st, y, y_ref,
-                       n, partial);
+    hipLaunchKernelGGL(diff_rows_kernel<false>, dim3((unsigned)rows), dim3(256), 0, st, y, ldy,
+                       y_ref, n, acc, partial);
   }
   return hipGetLastError();
 }

@@ -89,11 +89,13 @@ hipError_t launch_gemm_tile(const int8_t* xq, const float* s_x, const int8_t* wq
 
 // First-call check: write `bytes` of buf (evicts the operands from the caches).
 hipError_t launch_flush(void* buf, size_t bytes, hipStream_t st);
-// y_ref[rows, n] = x[:rows] . w_hat^T (+ bias) in fp32 (x, w_hat, bias, y in dt),
-// then partial[2r] = sum_c (y - y_ref)^2 and partial[2r + 1] = sum_c y_ref^2
-// (float64) for each row r < rows.
+// y_ref[rows, n] = x[:rows] . w_hat^T (+ bias) in fp32 (x, w_hat, bias, y in dt;
+// y rows ldy apart), then for each row r < rows: partial[2r] = sum_c (y - y_ref)^2
+// and partial[2r + 1] = sum_c y_ref^2 in float64, added to partial's values when
+// `accumulate` is set (a check over column chunks: w_hat, bias and y offset to
+// the chunk's first column, n its width).
 hipError_t launch_check_rows(const uint16_t* x, const uint16_t* w_hat, const uint16_t* bias,
-                             const uint16_t* y, int rows, int n, int k, DType dt, float* y_ref,
-                             double* partial, hipStream_t st);
+                             const uint16_t* y, int64_t ldy, int rows, int n, int k, DType dt,
+                             bool accumulate, float* y_ref, double* partial, hipStream_t st);
 
 }  // namespace convrot

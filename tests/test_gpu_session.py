@@ -112,3 +112,37 @@ def test_session_on_a_workload_shape():
         print(f"zimage-attn session: tile {tile}, check error {err:.4g}", flush=True)
         assert torch.equal(y.view(torch.int16), want.view(torch.int16))
         assert tile in TILES and err < 0.05 and not latched
+
+
+def test_check_over_column_chunks():
+    """At k = 16384 the session buffer holds the check's W_hat for 7936
+    weight rows at a time: n = 8256 takes two chunks (the second ragged), with
+    a bias; the check's error still equals the oracle's over all n columns,
+    and the first call allocates no device memory (the buffer was made by
+    convrot_session_create)."""
+    g, m, n, k = 256, 8, 8256, 16384
+    print(f"session check in column chunks {m}x{n}x{k}", flush=True)
+    rng = np.random.default_rng(21)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    wb = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    bias_b = synth.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    wq_ref, s_ref = oracle.quantize_weights(wb, g, SEED)
+    x, wq, bias_t = dev16(xb), torch.from_numpy(wq_ref).to(DEV), dev16(bias_b)
+    s_w = torch.tensor([s_ref], dtype=torch.float32, device=DEV)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    with cr.Session() as ses:
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        ses.linear(x, wq, s_w, g, SEED, bias_t, out=y)
+        torch.cuda.synchronize()
+        # a first call that allocated would take >= 256 MB + 2nk (528 MB) here
+        assert torch.cuda.mem_get_info()[0] >= free0 - (64 << 20)
+        tile, err, latched = ses.lookup(m, n, k, g)
+    y_bits = oracle.linear_int8(xb, wq_ref, s_ref, g, SEED, bias_b)[0]
+    assert np.array_equal(host_bits(y), y_bits)
+    y8 = oracle.to_f64(y_bits, "bf16")
+    w_hat = oracle.to_f64(oracle.dequant_derotate(wq_ref, s_ref, g, SEED), "bf16")
+    y_def = oracle.to_f64(xb, "bf16") @ w_hat.T + oracle.to_f64(bias_b, "bf16")[None, :]
+    want_err = oracle.rel_frobenius(y8, y_def)
+    assert abs(err - want_err) <= 1e-4 + 1e-3 * want_err, (err, want_err)
+    assert not latched and tile in TILES

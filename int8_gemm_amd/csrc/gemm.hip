@@ -18,10 +18,11 @@
 //     come in runs of 4 consecutive output columns;
 //   * K-step BK = 128 bytes when K % 128 == 0, else 64; an NS-deep ring of
 //     LDS stages filled by global_load_lds_dwordx4 (global -> LDS, no
-//     VGPRs); one barrier per K-step, right after which the copies of stage
-//     s+NS go into the slot of the stage s just read (every wave waits for
-//     its LDS reads before the barrier). With producer waves, only they
-//     issue copies and wait for them;
+//     VGPRs); one barrier per K-step, after which the copies of stage s+NS
+//     go into the slot of the stage s just read (every wave waits for its
+//     LDS reads before the barrier; with 8 waves, the two waves of a SIMD
+//     issue theirs at different points of the step). With producer waves,
+//     only they issue copies and wait for them;
 //   * LDS stage: rows of BK bytes, weights then activations; each copy
 //     instruction fills 1024 / BK rows; within a row the 16-byte chunks are
 //     XOR-swizzled by row (below), which makes the fragment reads free of
@@ -36,7 +37,14 @@
 // 128-byte K-step turns every request into a whole L2 line (+9-37% over 64
 // bytes, even with the ring cut to two stages; on the 192 tile only
 // together with four copy-issuing waves). Deeper rings, an L2 prefetch copy
-// and non-temporal output stores were all slower.
+// and non-temporal output stores were all slower. Every round of tiles
+// ends with all CUs writing their output tiles at once: with 256 x 256
+// tiles at K = 5120 that burst is ~9% of the time (skipping the stores in a
+// timing copy saves it). Persistent blocks that issue the next tile's first
+// copies before the stores did not hide it (a single vmcnt orders the next
+// tile's copy waits behind the stores) and were slower for their register
+// use; a 4-wave 256 x 256 layout (128 x 128 per wave, accumulators in
+// AGPRs) lost 12% for want of a second wave per SIMD.
 // Both operands are K-contiguous ("TN"). K % 64 == 0, N % 16 == 0.
 
 #include "common.h"
@@ -362,8 +370,14 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     if constexpr (NP == 0) wait_stage_runtime(min(LA - 2, nk - 2 - s));  // stage s+1 landed
     wait_lgkm0();  // this wave's reads of stage s are done before the barrier
     lds_barrier();
+    // With 8 waves, waves w and w + 4 share a SIMD: the first four issue
+    // their copies right after the barrier, the other four after the MFMAs
+    // of the last slice, so one wave of each SIMD keeps its MFMAs going
+    // while the other issues (all issuing at once left the MFMA pipes idle
+    // for the length of the issue, +1.5-5% measured).
+    const bool late = NP == 0 && NW == 8 && wave >= 4;
     if constexpr (NP == 0) {
-      if (s + LA < nk) issue(s + LA, (s + LA) % NS);
+      if (!late && s + LA < nk) issue(s + LA, (s + LA) % NS);
     }
     // Every step takes the same path, the last one included (its reads of
     // a stale ring slot land in X and are never used): with a branch around
@@ -373,6 +387,9 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     read_slice(s + 1, 0, xa, xb);
     mfma_slice(ya, yb);  // H is even: the last slice sits in Y
     sched_slice();
+    if constexpr (NP == 0) {
+      if (late && s + LA < nk) issue(s + LA, (s + LA) % NS);
+    }
   }
 
   // ---- epilogue: 32x32 output layout: lane holds m = lane % 32 of the

@@ -75,7 +75,7 @@ def _parse():
                          "passes, which time nothing, may set it to 0")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the FFN pair, its legs and the roofline GEMM (profiling runs)")
-    ap.add_argument("--leg", choices=("act_quant", "dequant", "gemm", "linear"),
+    ap.add_argument("--leg", choices=("act_quant", "dequant", "gemm", "linear", "vendor_gemm"),
                     help="instead of the headline line: time one leg of one workload "
                          "(--config, --g) over --steps launches (counter and trace runs)")
     ap.add_argument("--config", default="wan-ffn-up",
@@ -129,6 +129,12 @@ def _one_leg(args):
             units, unit = 3.0 * m * k + 4.0 * m, "GB/s"
         elif args.leg == "gemm":
             fn = lambda i: cr.convrot_gemm_int8(xq, sx, wq, s_w, y=ys[i % len(ys)])  # noqa: E731
+            units, unit = 2.0 * m * n * k, "TOPS"
+        elif args.leg == "vendor_gemm":
+            # reference point only: the platform's int8 GEMM (torch._int_mm, int32
+            # out, no scaling epilogue) on the same operands; not this library
+            wt = wq.t()
+            fn = lambda i: torch._int_mm(xq, wt)  # noqa: E731
             units, unit = 2.0 * m * n * k, "TOPS"
         else:
             fn = lambda i: cr.convrot_linear_int8(  # noqa: E731

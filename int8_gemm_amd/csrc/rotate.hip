@@ -265,6 +265,12 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       v[2 * i] = (double)(F16 ? half_lo(w[i]) : bf16lo(w[i]));
       v[2 * i + 1] = (double)(F16 ? half_hi(w[i]) : bf16hi(w[i]));
     }
+    // the next batch's words: in flight during the transform and the rest of
+    // this batch (the current words are dead once widened; issued here, the
+    // loads are 3-4% faster on 5120- and 13824-wide rows than issued after
+    // the transform)
+    uint32_t wn[32];
+    load(batch + gridDim.x, wn);
     fwht_inlane<G, CH>(v);
     if constexpr (G == 256) {
       const int q = c & 3;  // position of this lane's 64-element part in its group
@@ -333,10 +339,6 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       }
     }
 
-    // the next batch's words, in flight during the rest of this batch (the
-    // transform's float64 registers are free by now)
-    uint32_t wn[32];
-    load(batch + gridDim.x, wn);
     const int slot = it % 3;
     if (active) {
       atomicMax(&s_rowmax[slot][r_in], __float_as_uint(amax));

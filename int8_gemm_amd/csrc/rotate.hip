@@ -171,6 +171,11 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   __shared__ uint32_t s_rowunc[3][F16 ? 1 : 256];
   __shared__ uint32_t s_rowconf[3][F16 ? 1 : 256];
   __shared__ uint32_t s_open[F16 ? 1 : 4][F16 ? 1 : 512];
+  // g = 256: the byte masks of the sign step (0xFF where d = -1), per part q
+  // of a group and output word: the four parts differ, so in registers they
+  // would cost a lane 32 VGPRs, and rebuilt per word ~5 VALU instructions
+  __shared__ __attribute__((aligned(16))) uint32_t s_sgn[G == 256 ? 4 : 1][16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sgn1[G == 256 ? 4 : 1][16];  // & 0x01010101
 
   const int tid = threadIdx.x;
   const int r_in = tid / T;
@@ -225,7 +230,16 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
   uint32_t w[32];
   int64_t batch = blockIdx.x;
   load(batch, w);
-  __syncthreads();  // slot initialisation visible
+  if constexpr (G == 256) {
+    if (tid < 64) {
+      const int q = tid >> 4, d = tid & 15;
+      const uint32_t word = sm.w[2 * q + (d >> 3)];
+      const uint32_t m = nibble_to_bytemask((word >> ((4 * d) & 31)) & 0xFu);
+      s_sgn[q][d] = m;
+      s_sgn1[q][d] = m & 0x01010101u;
+    }
+  }
+  __syncthreads();  // slot and table initialisation visible
 
   int it = 0;
   for (; batch < nbatches; ++it, batch += gridDim.x) {
@@ -265,12 +279,13 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       v[2 * i] = (double)(F16 ? half_lo(w[i]) : bf16lo(w[i]));
       v[2 * i + 1] = (double)(F16 ? half_hi(w[i]) : bf16hi(w[i]));
     }
-    // the next batch's words: in flight during the transform and the rest of
-    // this batch (the current words are dead once widened; issued here, the
-    // loads are 3-4% faster on 5120- and 13824-wide rows than issued after
-    // the transform)
+    // The next batch's words, in flight during the rest of this batch. For
+    // g = 256 they are loaded here, while the transform runs (the current
+    // words are dead once widened): 3-4% faster on 5120- and 13824-wide rows
+    // than after the transform. For smaller groups after the transform (here
+    // they would cost spills: up to 19% slower at g = 4).
     uint32_t wn[32];
-    load(batch + gridDim.x, wn);
+    if constexpr (G == 256) load(batch + gridDim.x, wn);
     fwht_inlane<G, CH>(v);
     if constexpr (G == 256) {
       const int q = c & 3;  // position of this lane's 64-element part in its group
@@ -339,6 +354,7 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       }
     }
 
+    if constexpr (G != 256) load(batch + gridDim.x, wn);
     const int slot = it % 3;
     if (active) {
       atomicMax(&s_rowmax[slot][r_in], __float_as_uint(amax));
@@ -388,6 +404,24 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
         }
         if (c == 0) scale[row] = sc;
 
+        // sign masks of this lane's output words (g = 256: from the table)
+        uint32_t mk[16], mk1[16];
+        if constexpr (G == 256) {
+          const u4* tm = reinterpret_cast<const u4*>(s_sgn[c & 3]);
+          const u4* t1 = reinterpret_cast<const u4*>(s_sgn1[c & 3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u4 a = tm[i], b = t1[i];
+            mk[4 * i] = a.x; mk[4 * i + 1] = a.y; mk[4 * i + 2] = a.z; mk[4 * i + 3] = a.w;
+            mk1[4 * i] = b.x; mk1[4 * i + 1] = b.y; mk1[4 * i + 2] = b.z; mk1[4 * i + 3] = b.w;
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 16; ++d) {
+            mk[d] = nibble_to_bytemask(((d < 8 ? sg0 : sg1) >> ((4 * d) & 31)) & 0xFu);
+            mk1[d] = mk[d] & 0x01010101u;
+          }
+        }
         uint32_t outw[16];
 #pragma unroll
         for (int d = 0; d < 16; ++d) {
@@ -400,10 +434,8 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
           const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
           const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
           const uint32_t packed = t0 | t1;
-          const uint32_t nib = ((d < 8 ? sg0 : sg1) >> ((4 * d) & 31)) & 0xFu;
-          const uint32_t m = nibble_to_bytemask(nib);
           // negate the bytes with d = -1 (biased: 256 - v never carries), unbias
-          outw[d] = ((packed ^ m) + (m & 0x01010101u)) ^ 0x80808080u;
+          outw[d] = ((packed ^ mk[d]) + mk1[d]) ^ 0x80808080u;
         }
         u4* o = reinterpret_cast<u4*>(xq + row * (int64_t)K + (int64_t)CH * c);
 #pragma unroll

@@ -284,6 +284,19 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
     // words are dead once widened): 3-4% faster on 5120- and 13824-wide rows
     // than after the transform. For smaller groups after the transform (here
     // they would cost spills: up to 19% slower at g = 4).
+    // sum |x| over the lane (over its quad's group at g = 256), for the error
+    // bound of wide groups below
+    double sabs = 0.0;
+    if constexpr (!F16) {
+      if (wide_mask != 0u) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) sabs += fabs(v[i]);
+        if constexpr (G == 256) {
+          sabs += dpp_f64<kQuadXor1>(sabs);
+          sabs += dpp_f64<kQuadXor2>(sabs);
+        }
+      }
+    }
     uint32_t wn[32];
     if constexpr (G == 256) load(batch + gridDim.x, wn);
     fwht_inlane<G, CH>(v);
@@ -317,9 +330,15 @@ __global__ __launch_bounds__(512) void rotate_quant_fast_kernel(
       // u unless an open element's larger candidate could be the row's
       // absmax, or its two candidates quantize to different bytes (checked
       // once the scale is known). Wider intervals defer the row.
+      // The same bound from the computed sum of |x| (the lane's, which covers
+      // each of its groups; the whole group's at g = 256): S < 2^(e_S + 1)
+      // (1 + 2^-46) with e_S the exponent of the float64 sum, so
+      // 2^(e_S + ceil(log2 LOGG) - 51) is again twice the bound; the smaller
+      // of the two is used (tighter for groups with few large elements).
       constexpr int LL = LOGG <= 2 ? 1 : (LOGG <= 4 ? 2 : 3);
-      const double delta = __longlong_as_double(
-          (int64_t)(uint64_t)(emax_f + (uint32_t)(1023 - 127 + LL + LOGG - 51)) << 52);
+      const uint32_t fe = emax_f + (uint32_t)(1023 - 127 + LL + LOGG - 51);
+      const uint32_t fs = (uint32_t)((uint64_t)__double_as_longlong(sabs) >> 52) + (uint32_t)(LL - 51);
+      const double delta = __longlong_as_double((int64_t)(uint64_t)(fs < fe ? fs : fe) << 52);
       uint32_t om[2] = {0u, 0u}, um[2] = {0u, 0u};  // open elements; other candidate above u
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -503,6 +522,11 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
   __shared__ uint32_t s_rowflag[256];
   __shared__ uint32_t s_rowunc[256];   // 1 + bits of an undecided element's larger candidate
   __shared__ uint32_t s_rowconf[256];  // an undecided element quantizes both ways
+  // after the resolution of a row's absmax-risk elements: the row's absmax,
+  // its largest undecided candidate (+1), and a flag for an element too close
+  __shared__ uint32_t s_rowmax2[WIDE ? 256 : 1];
+  __shared__ uint32_t s_rowunc2[WIDE ? 256 : 1];
+  __shared__ uint32_t s_rowflag2[WIDE ? 256 : 1];
 
   const int tid = threadIdx.x;
   const int r_in = tid / T;
@@ -567,6 +591,11 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     s_rowflag[tid] = 0u;
     s_rowunc[tid] = 0u;
     s_rowconf[tid] = 0u;
+    if constexpr (WIDE) {
+      s_rowmax2[tid] = 0u;
+      s_rowunc2[tid] = 0u;
+      s_rowflag2[tid] = 0u;
+    }
   }
   if (mode == kRowDeferred) {
     // rows that the fast kernel finished are skipped as a whole
@@ -636,6 +665,7 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     uint32_t unc_hi = 0u;
     bool unsafe = false;
     float wamax = 0.0f;
+    float sabs_g = 0.0f;  // fp32 sum of |x| over the group (over the lane for g < 32)
     {
       double y[CH];
 #pragma unroll
@@ -657,7 +687,9 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
       if constexpr (LPG > 2) xstage(std::integral_constant<int, 2>{});
       if constexpr (LPG > 4) xstage(std::integral_constant<int, 4>{});
       static_assert(LPG <= 8, "group spans at most 8 lanes");
-      const double delta = (double)sabs * 0x1p-46;
+      sabs_g = sabs;
+      // twice the bound log2 g * 2^-53 * S <= 2^-50 S (sabs >= S (1 - 2^-16))
+      const double delta = (double)sabs * 0x1p-49;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         u[i] = (float)y[i];
@@ -686,10 +718,130 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
       if (umask != 0ull) atomicMax(&s_rowunc[r_in], unc_hi + 1u);
     }
     __syncthreads();
-    const float amax_u = __uint_as_float(s_rowmax[r_in]);
+    // ---- rows whose absmax an undecided element could be: those elements
+    // (larger candidate reaching the row's absmax) get their exact rounding,
+    // then the row takes its absmax again; the rest of the row is unchanged.
+    bool risky = false;
+    {
+      const uint32_t au0 = s_rowmax[r_in], ru0 = s_rowunc[r_in];
+      risky = active && s_rowflag[r_in] == 0u && ru0 != 0u && ru0 - 1u >= au0 &&
+              __uint_as_float(au0) <= 3.0e38f;
+      if (__syncthreads_or(risky)) {
+        uint64_t pend = 0ull;
+        if (risky) {
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            const uint32_t mb = __float_as_uint(u[i]) & 0x7FFFFFFFu;
+            const uint32_t hb = mb + (uint32_t)((dmask >> i) & 1ull);
+            pend |= (uint64_t)(((umask >> i) & 1ull) && hb >= au0) << i;
+          }
+        }
+        bool left = false;
+        // ---- the exact rounding of the undecided elements: per position i a
+        // group's lanes sum their part's inputs again with error-free
+        // additions (value s, rounding errors summed apart in e), then run the
+        // cross-lane stages on (s, e) the same way, so that every lane holds
+        // its own output at position i as s + e, within 2^-93 sum |x| of the
+        // exact sum. From r = RN32(s): if s + e lies farther than that margin
+        // from r's rounding boundaries it rounds to r; else, from the midpoint
+        // of r and its neighbour on the side of s + e, to one of the two.
+        // What is too close to decide leaves the row to the banded algorithm.
+        // The float64 differences used are exact (Sterbenz: the operands lie
+        // within a factor two of each other). ----
+        const double bnd = (double)sabs_g * 0x1p-88;  // margin for |s + e - exact| (sabs: fp32 group sum)
+        for (;;) {
+          uint32_t code = pend != 0ull ? (uint32_t)__builtin_ctzll(pend) : 0xFFFFu;
+          auto gmin = [&](auto mt) {
+            constexpr int m = decltype(mt)::value;
+            const uint32_t t = xor_lanes_u32<m>(code);
+            code = t < code ? t : code;
+          };
+          if constexpr (LPG > 1) gmin(std::integral_constant<int, 1>{});
+          if constexpr (LPG > 2) gmin(std::integral_constant<int, 2>{});
+          if constexpr (LPG > 4) gmin(std::integral_constant<int, 4>{});
+          if (__ballot(code != 0xFFFFu) == 0ull) break;  // wave-uniform exit
+          if (code == 0xFFFFu) continue;                  // uniform over the group's lanes
+          const int i = (int)code;
+          const int gb = G >= CH ? 0 : (i / G) * G;  // first element of the element's group
+          const int jj = i - gb;                      // position within this lane's part
+          double ps = 0.0, pe = 0.0;
+  #pragma unroll
+          for (int k = 0; k < CH; ++k) {
+            if (G < CH && (k < gb || k >= gb + G)) continue;
+            const double xk =
+                (double)__uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+            const double tk = (__builtin_popcount((uint32_t)(jj & (k - gb))) & 1) ? -xk : xk;
+            const double sn = ps + tk;
+            const double bb = sn - ps;
+            pe += (ps - (sn - bb)) + (tk - bb);
+            ps = sn;
+          }
+          auto tstage = [&](auto mt) {
+            constexpr int m = decltype(mt)::value;
+            const double os = xor_lanes_f64<m>(ps), oe = xor_lanes_f64<m>(pe);
+            const bool hi_lane = (c & m) != 0;  // the difference: partner - own
+            const double a = hi_lane ? os : ps, b = hi_lane ? -ps : os;
+            const double sn = a + b;
+            const double bb = sn - a;
+            pe = (hi_lane ? oe - pe : pe + oe) + ((a - (sn - bb)) + (b - bb));
+            ps = sn;
+          };
+          if constexpr (LPG > 1) tstage(std::integral_constant<int, 1>{});
+          if constexpr (LPG > 2) tstage(std::integral_constant<int, 2>{});
+          if constexpr (LPG > 4) tstage(std::integral_constant<int, 4>{});
+          if ((pend >> i) & 1ull) {
+            const float r = (float)ps;
+            const uint32_t rb = __float_as_uint(r);
+            uint32_t ef = (rb >> 23) & 0xFFu;
+            ef = ef < 1u ? 1u : ef;
+            const uint32_t pow2 = (rb & 0x7FFFFFu) == 0u ? 1u : 0u;
+            const double h =
+                __longlong_as_double((int64_t)(uint64_t)(ef + (1023u - 151u) - pow2) << 52);
+            const double d = (ps - (double)r) + pe;
+            float un = r;
+            bool ok = fabs(ps) <= 3.0e38;
+            if (ok && !(fabs(d) + (bnd + h * 0x1p-50) < h)) {
+              // between r and its neighbour on the side of d
+              const uint32_t up = rb == 0x80000000u ? 1u : ((rb >> 31) ? rb - 1u : rb + 1u);
+              const uint32_t dn = rb == 0u ? 0x80000001u : ((rb >> 31) ? rb + 1u : rb - 1u);
+              const float nb = __uint_as_float(d > 0.0 ? up : dn);
+              const double mid = 0.5 * ((double)r + (double)nb);
+              const double dd = (ps - mid) + pe;
+              ok = r != 0.0f && nb != 0.0f && (r > 0.0f) == (nb > 0.0f) && fabs(dd) > 2.0 * bnd;
+              un = (dd > 0.0) == (nb > r) ? nb : r;
+            }
+            if (ok) {
+  #pragma unroll
+              for (int e2 = 0; e2 < CH; ++e2) u[e2] = e2 == i ? un : u[e2];
+              umask &= ~(1ull << i);
+              dmask &= ~(1ull << i);
+            } else {
+              left = true;
+            }
+            pend &= ~(1ull << i);
+          }
+        }
+        if (risky) {
+          float am2 = 0.0f;
+          uint32_t un2 = 0u;
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            am2 = fmaxf(am2, fabsf(u[i]));
+            const uint32_t mb = __float_as_uint(u[i]) & 0x7FFFFFFFu;
+            const uint32_t hb = ((umask >> i) & 1ull) ? mb + (uint32_t)((dmask >> i) & 1ull) : 0u;
+            un2 = hb > un2 ? hb : un2;
+          }
+          atomicMax(&s_rowmax2[r_in], __float_as_uint(am2));
+          if (left) atomicOr(&s_rowflag2[r_in], 1u);
+          if (umask != 0ull) atomicMax(&s_rowunc2[r_in], un2 + 1u);
+        }
+        __syncthreads();
+      }
+    }
+    const float amax_u = __uint_as_float(risky ? s_rowmax2[r_in] : s_rowmax[r_in]);
     const float amax_x = amax_u * (1.0f / (float)(1 << KS));  // exact when not deferred
-    const uint32_t rowunc = s_rowunc[r_in];
-    bool wide_ok = active && s_rowflag[r_in] == 0u && amax_u <= 3.0e38f &&
+    const uint32_t rowunc = risky ? s_rowunc2[r_in] : s_rowunc[r_in];
+    bool wide_ok = active && (risky ? s_rowflag2[r_in] : s_rowflag[r_in]) == 0u && amax_u <= 3.0e38f &&
                    !(amax_u > 0.0f && amax_x < 0x1p-100f) &&
                    !(rowunc != 0u && rowunc - 1u >= __float_as_uint(amax_u));
     float wsc = 0.0f;

@@ -3,9 +3,11 @@
 Rows with a group whose exponents span too widely for exact float64 sums are
 first transformed once in float64 (butterflies, depth log2 g). The pass keeps
 an element when |y - RN32(y)| + delta stays below the half-gap h from RN32(y)
-to its next rounding boundary, with delta = 2^-46 * (fp32 sum of |x|). This
-test checks, with exact integer arithmetic (every bf16 value is a multiple of
-2^-133), that
+to its next rounding boundary, with delta = 2^-49 * (fp32 sum of |x|); the
+fast kernel uses the smaller of 2^(E + ceil(log2 log2 g) + log2 g - 51) (E the
+group's largest exponent) and 2^(e_S + ceil(log2 log2 g) - 51) (e_S the
+exponent of the float64 sum of |x|). This test checks, with exact integer
+arithmetic (every bf16 value is a multiple of 2^-133), that
 
   * the float64 transform's error never exceeds log2(g) * 2^-53 * sum |x|;
   * an accepted element always equals the correctly rounded fp32 value of the
@@ -114,7 +116,19 @@ def test_float64_transform_bound_and_acceptance_rule():
             s32 = np.float32(0)
             for t in np.abs(x):
                 s32 = np.float32(s32 + t)
-            delta = float(s32) * 2.0 ** -46
+            # the deferred pass's margin, and the fast kernel's (which must
+            # never be the looser one here: both are twice the bound)
+            delta = float(s32) * 2.0 ** -49
+            logg = int(math.log2(g))
+            ll = 1 if logg <= 2 else (2 if logg <= 4 else 3)
+            emax = max(math.frexp(float(t))[1] - 1 for t in x if t != 0)
+            s64 = 0.0
+            for t in np.abs(x):
+                s64 += float(t)
+            e_s = math.frexp(s64)[1] - 1
+            fast_delta = min(2.0 ** (emax + ll + logg - 51), 2.0 ** (e_s + ll - 51))
+            bound = math.log2(g) * 2.0 ** -53 * s_abs
+            assert delta > bound and fast_delta > bound, (g, delta, fast_delta, bound)
             for j in range(g):
                 yj = to_int(y[j])
                 assert yj is not None

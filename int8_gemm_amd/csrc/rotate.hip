@@ -9,17 +9,24 @@
 //   * Fast kernel: if a group's nonzero elements span at most 45 - log2(g)
 //     binades, every butterfly partial sum is a multiple of the smallest
 //     element's quantum and below g times the largest element, so it fits
-//     53 bits and float64 is exact. Rows holding a group outside that bound
-//     (or rows too small for the folded scaling below) are left to the exact
-//     kernel: their scale slot receives the kDeferredRow NaN.
+//     53 bits and float64 is exact. A group outside that bound ("wide") gets
+//     an error bound instead (from its largest exponent and its sum of |x|):
+//     an output whose bound interval rounds to one fp32 is decided, the
+//     others are "open" between two neighbouring floats. The row is finished
+//     unless an open element could be its absmax, has more than two
+//     candidates, or quantizes differently for its two candidates; such rows
+//     (and rows too small for the folded scaling below) are left to the
+//     exact kernel: their scale slot receives the kDeferredRow NaN.
 //   * Deferred rows (the exact kernel's deferred mode) first get one rounded
 //     float64 transform: each output is within log2(g) * 2^-53 * sum|x| of
 //     the exact sum (a depth-log2(g) tree of rounded additions), so with
 //     that bound (and margin) an element either provably rounds to
-//     RN32(y), or to one of RN32(y) and its neighbour. The row is finished
-//     there unless such an undecided element could be the row's absmax or
-//     quantizes differently for its two candidates (ties decided only by
-//     elements the float64 sum lost: GELU-tailed activations).
+//     RN32(y), or to one of RN32(y) and its neighbour. The undecided
+//     elements that could be the row's absmax are then summed again with
+//     error-free additions, which decides nearly all of them. The row is
+//     finished there unless an undecided element is still a candidate for
+//     the absmax or quantizes differently for its two candidates (ties
+//     decided only by elements the float64 sum lost).
 //   * Exact kernel: splits each group's elements into bands of kBand
 //     binades (each band's transform is exact in float64), turns each band's
 //     sums into integers of the band's quantum and adds the bands bottom-up
@@ -689,11 +696,12 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
     // ---- one rounded float64 transform first (rows the fast kernel left:
     // mostly wide-span groups). Each output is a depth-LOGG tree of correctly
     // rounded additions, so it is within LOGG * 2^-53 * S of the exact sum
-    // (S = sum |x| over the group); delta = 2^-46 * S' bounds that with a wide
-    // margin (S' = fp32 sum of |x| over the group for g >= 32, over the lane
-    // otherwise). With u = RN32(y) and d = y - u (exact), the exact sum rounds
-    // to u when |d| + delta is below the half-gap h from u to its next
-    // rounding boundary (ulp/2, ulp/4 at a power of two, 2^-151 at zero);
+    // (S = sum |x| over the group); delta = 2^-49 * S' is at least twice that
+    // (LOGG <= 8; S' = fp32 sum of |x| over the group for g >= 32, over the
+    // lane otherwise, S' >= S (1 - 2^-16)). With u = RN32(y) and d = y - u
+    // (exact), the exact sum rounds to u when |d| + delta is below the
+    // half-gap h from u to its next rounding boundary (ulp/2, ulp/4 at a
+    // power of two, 2^-151 at zero);
     // h is a power of two, so the float64 test is exact. Otherwise, with
     // delta < h, it rounds to u or to u's neighbour on the side of y
     // (undecided). The row is finished here unless an undecided element

@@ -256,6 +256,19 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     }
   };
 
+  // The epilogue's row scales (and the per-tensor weight scale), loaded
+  // before the first copies instead of after the K-loop, where their
+  // latency stood between the last MFMAs and the stores of every tile.
+  // Issued ahead of the copies, they complete first (in-order vmcnt), so the
+  // stage waits account for them.
+  float sx_pre[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int m = m0 + wm * WTM + j * 32 + (lane & 31);
+    sx_pre[j] = s_x[m < M ? m : M - 1];
+  }
+  const float sw_pre = PC ? 0.0f : *s_w;
+
   if constexpr (NP > 0) {
     if (wave >= NW) {
       // ---- producer: stage s+1 landed before the barrier that ends step
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
   // complete before the K-loop. A scalar load still in flight at the loop
   // entry (they return out of order) makes every LDS-read wait in the loop
   // a full lgkmcnt(0) drain.
-  asm volatile("" ::"s"(y), "s"(acc_out), "s"(s_x), "s"(s_w), "s"(bias));
+  asm volatile("" ::"s"(y), "s"(acc_out), "s"(s_x), "s"(s_w), "s"(bias), "s"(sw_pre));
   if constexpr (NP == 0) wait_stage_runtime(min(LA - 1, nk - 1));  // stage 0 landed
   lds_barrier();
   read_slice(0, 0, xa, xb);
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     wait_lgkm0();  // every wave's last ring reads are done before the tile is staged
     lds_barrier();
   }
-  const float sw = PC ? 0.0f : *s_w;
+  const float sw = sw_pre;
   // per-channel: the 4 consecutive columns of each (i, a) register group,
   // loaded once for all NJ row blocks
   typedef float f4 __attribute__((ext_vector_type(4)));
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP), MINB) void gemm_i8_kernel(
     const int ml = wm * WTM + j * 32 + fr;  // row within the tile
     const int m = m0 + ml;
     if (m >= M) continue;
-    const float sx = s_x[m];
+    const float sx = sx_pre[j];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll

@@ -811,12 +811,18 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
           const int gb = G >= CH ? 0 : (i / G) * G;  // first element of the element's group
           const int jj = i - gb;                      // position within this lane's part
           double ps = 0.0, pe = 0.0;
-          // the part's inputs again, 8 at a time from memory (keeps the
-          // registers of the packed words free)
+          // the part's inputs again from memory (the packed words' registers
+          // stay free through the transform): for groups across lanes all four
+          // loads in flight at once (the loop's latency decides the pass on
+          // GELU-tailed rows), for in-lane groups 8 at a time (registers)
+          constexpr int NQ8 = G >= 64 ? CH / 8 : 1;
           const uint4* xp = reinterpret_cast<const uint4*>(x + row * (int64_t)K + (int64_t)CH * c);
-#pragma unroll 1
+          uint4 q4[NQ8];
+#pragma unroll
+          for (int b = 0; b < NQ8; ++b) q4[b] = xp[b];
+#pragma unroll(NQ8)
           for (int k0 = 0; k0 < CH; k0 += 8) {
-            const uint4 q8 = xp[k0 >> 3];
+            const uint4 q8 = G >= 64 ? q4[(k0 >> 3) % NQ8] : xp[k0 >> 3];
             const uint32_t w4[4] = {q8.x, q8.y, q8.z, q8.w};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {

@@ -749,13 +749,15 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
         const double d = y[i] - (double)u[i];
         const bool wide = (gmask >> (i / GE)) & 1u;
         const bool und = wide && !(fabs(d) + delta < h);
-        unsafe |= und && !(delta < h);
-        const uint32_t mb = rb & 0x7FFFFFFFu;
-        const bool away = (d > 0.0) == !(rb >> 31) || mb == 0u;
-        umask |= (uint64_t)und << i;
-        dmask |= (uint64_t)(und && away) << i;
-        const uint32_t hb = und ? mb + (away ? 1u : 0u) : 0u;
-        unc_hi = hb > unc_hi ? hb : unc_hi;
+        if (und) {  // rare: the bookkeeping of an undecided element
+          unsafe |= !(delta < h);
+          const uint32_t mb = rb & 0x7FFFFFFFu;
+          const bool away = (d > 0.0) == !(rb >> 31) || mb == 0u;
+          umask |= 1ull << i;
+          dmask |= (uint64_t)away << i;
+          const uint32_t hb = mb + (away ? 1u : 0u);
+          unc_hi = hb > unc_hi ? hb : unc_hi;
+        }
       }
     }
     if (active) {
@@ -925,14 +927,16 @@ __global__ __launch_bounds__(512) void rotate_quant_exact_kernel(
           const int j = (G >= CH) ? base_j + i : (i % G);
           const float sgn = sign_bit(sm, j) ? -1.0f : 1.0f;
           b[e] = __float_as_uint((sgn * u[i]) * inv_u + kQuantPlain);
-          // the other candidate of an undecided element (u's sign; a zero's
-          // sign does not reach q)
-          const uint32_t rb = __float_as_uint(u[i]);
-          const uint32_t mb = rb & 0x7FFFFFFFu;
-          const uint32_t nb = ((dmask >> i) & 1ull) ? mb + 1u : mb - 1u;
-          const float un = __uint_as_float((rb & 0x80000000u) | nb);
-          const uint32_t b2 = __float_as_uint((sgn * un) * inv_u + kQuantPlain);
-          conflict |= ((umask >> i) & 1ull) && ((b[e] ^ b2) & 0xFFu) != 0u;
+          if ((umask >> i) & 1ull) {
+            // the other candidate of an undecided element (u's sign; a zero's
+            // sign does not reach q)
+            const uint32_t rb = __float_as_uint(u[i]);
+            const uint32_t mb = rb & 0x7FFFFFFFu;
+            const uint32_t nb = ((dmask >> i) & 1ull) ? mb + 1u : mb - 1u;
+            const float un = __uint_as_float((rb & 0x80000000u) | nb);
+            const uint32_t b2 = __float_as_uint((sgn * un) * inv_u + kQuantPlain);
+            conflict |= ((b[e] ^ b2) & 0xFFu) != 0u;
+          }
         }
         const uint32_t t0 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
         const uint32_t t1 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);

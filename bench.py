@@ -230,12 +230,15 @@ def _events_time(fn, reps, stream, batches=3):
 class ClockSampler:
     """Shader clock (MHz, mean over the XCDs) and socket power (W) sampled
     through amdsmi from a background thread while GPU work runs. The
-    firmware refreshes the figures every few tens of ms; samples taken before
-    `settle_s` are dropped (the clocks ramp up under load)."""
+    firmware refreshes the figures every few tens of ms, on some boxes far
+    more rarely: a reading equal to the one before it is a repeat of a
+    stale figure and is dropped; so are readings taken before `settle_s`
+    (the clocks ramp up under load)."""
 
-    def __init__(self, settle_s=0.3, period_s=0.02):
+    def __init__(self, settle_s=0.5, period_s=0.02):
         self.settle_s, self.period_s = settle_s, period_s
         self.samples, self.error = [], None
+        self._last, self.reads = None, 0
         self._stop = threading.Event()
         self._handle = None
         try:
@@ -264,8 +267,13 @@ class ClockSampler:
                 clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
                 clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
                 pw = m.get("current_socket_power")
-                if t >= self.settle_s and isinstance(clk, (int, float)):
-                    self.samples.append((clk, pw if isinstance(pw, (int, float)) else None))
+                pw = pw if isinstance(pw, (int, float)) else None
+                if isinstance(clk, (int, float)):
+                    fresh = self._last is None or (clk, pw) != self._last
+                    self._last = (clk, pw)
+                    self.reads += 1
+                    if t >= self.settle_s and fresh:
+                        self.samples.append((clk, pw))
             except Exception as e:  # noqa: BLE001
                 self.error = f"amdsmi read failed: {e!r}"[:200]
                 return
@@ -292,8 +300,9 @@ class ClockSampler:
         return {"sclk_MHz": round(clks[len(clks) // 2], 1),
                 "sclk_MHz_range": [round(clks[0], 1), round(clks[-1], 1)],
                 "socket_power_W": pws[len(pws) // 2] if pws else None,
-                "samples": len(clks), "source": "amdsmi gpu_metrics current_gfxclks (mean "
-                                                "over XCDs), median of samples under load"}
+                "samples": len(clks), "reads": self.reads,
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), median of the "
+                          "fresh readings under load (repeats of a reading dropped)"}
 
 
 # ---------------------------------------------------------------------------
@@ -567,8 +576,8 @@ def main():
     gemm_ms = _events_time(lambda i: cr.convrot_gemm_int8(xq1, sx1, wq1, sw1, y=y1), reps, stream)
     sampler = ClockSampler()
 
-    def clock_run():  # ~1 s of the same GEMM while the sampler reads the clock
-        for i in range(max(1, int(1000.0 / max(gemm_ms, 1e-3)))):
+    def clock_run():  # ~2 s of the same GEMM while the sampler reads the clock
+        for i in range(max(1, int(2000.0 / max(gemm_ms, 1e-3)))):
             cr.convrot_gemm_int8(xq1, sx1, wq1, sw1, y=y1)
             if i % 50 == 49:
                 torch.cuda.synchronize()

@@ -503,8 +503,14 @@ hipError_t launch_cfg(const int8_t* xq, const float* s_x, const int8_t* wq, cons
 // 384 x 192 tile exists for K % 128 == 0 only.
 TileCfg choose_tile(int64_t m, int64_t n, int64_t k, int cus) {
   const TileCfg cands[] = {{384, 192, 2, 1}, {256, 256, 2, 1}, {192, 192, 3, 1}, {128, 128, 2, 2}};
-  // duration of one full round relative to the 192 tile's (4608-row layers)
-  const double round_t[] = {1.75, 1.336, 1.0, 1.0};
+  // duration of one full round relative to the 192 tile's. Measured on MI355X
+  // the ratios vary with the shape (384 x 192: 1.71-1.85, 256 x 256:
+  // 1.25-1.56 of a 192 round; their ratio 1.18-1.37): the 384 figure is set
+  // to 1.2 times the 256 one, which orders the two tiles right on the
+  // workload layers and the linear's slices of them (e.g. 5112 x 13824 x
+  // 5120: 384 x 192 in 4 rounds 319 us, 256 x 256 in 4 rounds plus 56 tiles
+  // 338 us; 4608 x 3072 x 12288: 256 x 256 148 us, 384 x 192 152 us).
+  const double round_t[] = {1.6, 1.336, 1.0, 1.0};
   TileCfg best = cands[2];
   double best_t = 1e300;
   for (int c = 0; c < 4; ++c) {

@@ -304,7 +304,7 @@ def test_launch_plans_follow_compute_units(lib, cus):
 def test_gemm_tile_choice_counts_rounds_over_the_cus(lib):
     """The 384 x 192 tile covers 4608 x 3840 in 240 tiles, one round on 256
     CUs; on 128 CUs that takes two rounds, where the 256 x 256 tile's 270
-    tiles take three and the 192 tile's 480 four (a 384 x 192 round lasts 1.75
+    tiles take three and the 192 tile's 480 four (a 384 x 192 round lasts 1.6
     of a 192 round, a 256 round 1.336): the 384 tile stays the choice."""
     for cus in (256, 128):
         p = cr.convrot_plan_launch("gemm", m=4608, n=3840, k=3840, compute_units=cus)
@@ -316,6 +316,19 @@ def test_gemm_tile_choice_counts_rounds_over_the_cus(lib):
     # tiles win on round count
     p1 = cr.convrot_plan_launch("gemm", m=4096, n=4096, k=4096, compute_units=1)
     assert p1["tile_m"] in (256, 384)
+
+
+def test_gemm_tile_choice_on_the_workload_layers_and_slices(lib):
+    """The tile the chooser takes on 256 CUs for each workload layer and for
+    the token slices the linear cuts them into (at most 2N rows), as measured
+    fastest on an MI355X (HIP events, every tile forced in turn)."""
+    want = {(4608, 3840, 3840): 384, (4608, 12288, 3072): 384, (4608, 3072, 12288): 256,
+            (32760, 13824, 5120): 256, (27648, 13824, 5120): 256, (5112, 13824, 5120): 384,
+            (32760, 5120, 13824): 256, (10240, 5120, 13824): 384, (2040, 5120, 13824): 256,
+            (16384, 9216, 3072): 256}
+    for (m, n, k), tile in want.items():
+        p = cr.convrot_plan_launch("gemm", m=m, n=n, k=k, compute_units=256)
+        assert p["tile_m"] == tile, (m, n, k)
 
 
 def test_plan_launch_checks_shapes(lib):

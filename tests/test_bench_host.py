@@ -1,7 +1,8 @@
 """bench.py's contract on the CPU: the one-GPU refusal happens before anything
 touches a GPU, the options exist, the CPU-baseline leg reports the fields the
-JSON line carries, and the HBM traffic figure is only taken from a counter
-summary made on the current GEMM source."""
+JSON line carries, the HBM traffic figure is only taken from a counter
+summary made on the current GEMM source, and the clock sampler keeps fresh
+readings only."""
 
 import json
 import os
@@ -58,3 +59,38 @@ def test_traffic_only_for_the_current_gemm_source(tmp_path, monkeypatch):
     assert bench._traffic(1) is None
     f.write_text("not json")
     assert bench._traffic(1) is None
+
+
+def test_clock_sampler_keeps_fresh_readings_only():
+    """A firmware figure that repeats is stale: only readings that differ
+    from the one before them (after the settle time) enter the median."""
+    class FakeSmi:
+        def __init__(self, seq):
+            self.seq, self.i = seq, 0
+
+        def amdsmi_get_gpu_metrics_info(self, handle):
+            clk, pw = self.seq[min(self.i, len(self.seq) - 1)]
+            self.i += 1
+            return {"current_gfxclks": [clk] * 8, "current_socket_power": pw}
+
+    s = bench.ClockSampler.__new__(bench.ClockSampler)
+    s.settle_s, s.period_s = 0.0, 0.0
+    s.samples, s.error, s._last, s.reads = [], None, None, 0
+    seq = [(2100, 800)] * 5 + [(1700, 1350)] + [(1700, 1350)] * 3 + [(1750, 1340)] + [(1650, 1380)] * 4
+    s._amdsmi, s._handle = FakeSmi(seq), object()
+    s._stop = bench.threading.Event()
+    calls = {"n": 0}
+    real_wait = s._stop.wait
+
+    def stop_after(timeout):  # end the loop once the sequence is read
+        calls["n"] += 1
+        if calls["n"] >= len(seq):
+            s._stop.set()
+        return real_wait(0)
+
+    s._stop.wait = stop_after
+    s._run()
+    got = s.summary()
+    assert s.reads == len(seq)
+    assert [c for c, _ in s.samples] == [2100, 1700, 1750, 1650]
+    assert got["sclk_MHz"] == 1750 and got["samples"] == 4

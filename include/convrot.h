@@ -393,7 +393,7 @@ convrot_status convrot_rotation_signs(uint64_t rot_seed, int g, int8_t* d);
  *   Shape errors as for the corresponding entry point. */
 typedef enum convrot_kernel {
   CONVROT_KERNEL_ACT_QUANT = 0,          /* activation rotate + quantize, fast kernel   */
-  CONVROT_KERNEL_ACT_QUANT_DEFERRED = 1, /* its pass over the rows it defers            */
+  CONVROT_KERNEL_ACT_QUANT_DEFERRED = 1, /* its blocks' pass over the rows they defer   */
   CONVROT_KERNEL_EXACT = 2,              /* exact kernel (weights, the _exact hook)     */
   CONVROT_KERNEL_DEQUANT = 3,            /* dequant + derotate                          */
   CONVROT_KERNEL_GEMM = 4                /* int8 GEMM, automatic tile                   */

@@ -73,8 +73,4 @@ __device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
   return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
 }
 
-__device__ __forceinline__ bool sign_bit(const SignMask& s, int i) {
-  return (s.w[i >> 5] >> (i & 31)) & 1u;
-}
-
 }  // namespace convrot

@@ -279,14 +279,19 @@ def test_header_compiles_and_links_as_c99(lib, tmp_path):
 def test_launch_plans_follow_compute_units(lib, cus):
     """Persistent grids hold at most a fixed number of workgroups per CU, the
     GEMM's tile order spreads over CUs / 32 XCDs, and a plan covers the shape."""
-    # act-quant at K = 3840: one 60-lane row per 1-wave block, 8 per CU
+    # act-quant at K = 3840: two 60-lane rows per 2-wave block, 4 per CU
+    # (a block holds at least two rows, i.e. one row of the exact pass's
+    # 120-lane team for the rows it defers)
     p = cr.convrot_plan_launch("act_quant", m=4608, k=3840, g=256, compute_units=cus)
-    assert p["compute_units"] == cus and p["block"] == 64 and p["rows_per_block"] == 1
-    assert p["grid"] == min(4608, 8 * cus)
-    assert p["grid"] * p["passes"] >= 4608 > p["grid"] * (p["passes"] - 1)
-    # deferred rows at K = 12288: 6-wave rows, one block per CU
+    assert p["compute_units"] == cus and p["block"] == 128 and p["rows_per_block"] == 2
+    assert p["grid"] == min(4608 // 2, 4 * cus)
+    assert p["grid"] * p["passes"] >= 2304 > p["grid"] * (p["passes"] - 1)
+    # deferred rows: the fast kernel's grid and blocks, one 384-lane exact row
+    # per step at K = 12288 (two 192-lane fast rows in a 6-wave block)
     p = cr.convrot_plan_launch("act_quant_deferred", m=4608, k=12288, g=256, compute_units=cus)
-    assert p["block"] == 384 and p["grid"] == min(4608, cus)
+    f = cr.convrot_plan_launch("act_quant", m=4608, k=12288, g=256, compute_units=cus)
+    assert p["block"] == f["block"] == 384 and p["grid"] == f["grid"] == min(2304, cus)
+    assert f["rows_per_block"] == 2 and p["rows_per_block"] == 1 and p["passes"] == f["passes"]
     # dequant: 2 blocks per CU at g = 256, 4 at g <= 64
     for g, per_cu in ((256, 2), (64, 4), (4, 4)):
         p = cr.convrot_plan_launch("dequant", n=3840, k=3840, g=g, compute_units=cus)

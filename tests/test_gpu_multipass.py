@@ -1,10 +1,11 @@
 """Every pass of the persistent grids against the oracle, element by element.
 
-The act-quant kernels (fast and deferred-row), the exact kernel and the
-dequant walk their work in persistent workgroups, each taking batch i,
-i + grid, i + 2 grid, ... with the next batch prefetched into registers and
-per-batch LDS slots used round-robin. At the reduced test shapes one pass
-covers everything, so:
+The act-quant kernel, the exact kernel and the dequant walk their work in
+persistent workgroups, each taking batch i, i + grid, i + 2 grid, ... with
+the next batch prefetched into registers and per-batch LDS slots used
+round-robin; after its last batch an act-quant workgroup resolves the rows it
+deferred (batches marked in an LDS bitmap of 2048 passes, later ones by one
+flag). At the reduced test shapes one pass covers everything, so:
 
 * the first tests shrink the grids through convrot_set_compute_units (a
   process-wide test hook; sizing changes speed, never results) until every
@@ -138,9 +139,10 @@ def test_device_grid_fast_kernel_several_passes():
 
 
 def test_device_grid_deferred_pass_several_passes():
-    """GELU-tailed rows at K = 12288 are deferred by the fast kernel; 1100 of
-    them make the deferred-row pass walk several batches per workgroup on the
-    device's grid; every row compared, and the forward on every row."""
+    """GELU-tailed rows at K = 12288, some of which the fast kernel defers:
+    1100 rows give each workgroup of the device's grid several batches, so
+    the rows a workgroup resolves after its last batch come from several of
+    them; every row compared, and the forward on every row."""
     layer, g = synth.FLUX_MLP_DOWN.scaled(m=1100, n=256), 256
     passes = _device_passes("act_quant_deferred", m=layer.m, k=layer.k, g=g)
     print(f"device grid: deferred 1100x12288 passes {passes}", flush=True)
@@ -157,3 +159,39 @@ def test_device_grid_deferred_pass_several_passes():
     y = cr.convrot_linear_int8(x, wq, s_w, g, SEED)
     assert np.array_equal(host_bits(y),
                           oracle.epilogue(oracle.gemm_int32(xq_ref, wq_ref), s_ref, sx_ref))
+
+
+@pytest.mark.parametrize("few_cus", [1], indirect=True)
+def test_deferred_rows_past_the_pass_bitmap(few_cus):
+    """Rows whose absmax lies below the fast kernel's scaling range (elements
+    near 2^-110) are always deferred. At K = 256 on a one-CU grid every
+    workgroup walks 2100 batches, so such rows sit in the bitmap's first and
+    last words and past it (passes 2048 and later, found by the flag); those
+    rows and a sample of the others against the oracle, and no row is left
+    with the deferred marker."""
+    g, k = 256, 256
+    plan = cr.convrot_plan_launch("act_quant", m=1 << 20, k=k, g=g)
+    grid, rpb = plan["grid"], plan["rows_per_block"]
+    passes = 2100
+    m = grid * rpb * passes
+    print(f"deferred past the bitmap: grid {grid} rows/block {rpb} m {m}", flush=True)
+    assert cr.convrot_plan_launch("act_quant", m=m, k=k, g=g)["passes"] == passes
+    rng = np.random.default_rng(7)
+    xf = rng.standard_normal((m, k), dtype=np.float32)
+    tiny = []
+    for b in sorted({0, grid - 1, grid // 2}):
+        for p in (0, 5, 31, 32, 2047, 2048, 2049, passes - 1):
+            tiny.append((b + p * grid) * rpb + (p % rpb))
+    tiny = np.array(sorted(set(tiny)))
+    xf[tiny] *= np.float32(2.0 ** -110)
+    xb = synth.f32_to_bf16_bits(xf)
+    del xf
+    xq, sx = cr.convrot_quantize_activations(dev_bf16(xb), g, SEED)
+    sx_h = sx.cpu().numpy()
+    assert not np.isnan(sx_h).any()
+    rest = np.setdiff1d(rng.choice(m, 3000, replace=False), tiny)
+    rows = np.concatenate([tiny, rest])
+    xq_ref, sx_ref = oracle.quantize_activations(xb[rows], g, SEED)
+    assert np.array_equal(f32_bits(sx_h[rows]), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy()[rows], xq_ref)
+    assert (sx_h[tiny] < 2.0 ** -100).all()

@@ -5,6 +5,8 @@ format / scale / bias combination; the larger calls need several slices of the
 library's 64 MiB per-device scratch, GELU-tailed rows take the deferred-row
 pass through it. The call must not allocate through torch either."""
 
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -55,9 +57,18 @@ def _check_layer(layer, dtype, per_channel, with_bias):
     want = cr.convrot_linear_int8_ex(x, wq, s_w, 256, SEED, bias, per_channel=per_channel)
     out = torch.full_like(want, float("nan"))
     torch.cuda.synchronize()
+    # nothing allocated through torch: the garbage collector stays off around
+    # the call, so that it cannot free an earlier test's tensors meanwhile
+    gc.collect()
     before = torch.cuda.memory_allocated()
-    cr.convrot_linear_int8_noalloc(x, wq, s_w, 256, SEED, bias, per_channel=per_channel, out=out)
-    assert torch.cuda.memory_allocated() == before  # nothing allocated through torch
+    gc.disable()
+    try:
+        cr.convrot_linear_int8_noalloc(x, wq, s_w, 256, SEED, bias, per_channel=per_channel,
+                                       out=out)
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
+    assert after == before
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out), _bits(want)), layer.name
 

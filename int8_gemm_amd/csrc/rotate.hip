@@ -1237,9 +1237,11 @@ LaunchPlan plan_rotate(int64_t rows, int T, int wpc, int cus, int min_rows) {
 template <int G>
 hipError_t launch_fast(const uint16_t* x, int8_t* xq, float* s, int64_t rows, int K,
                        const SignMask& sm, bool f16, hipStream_t st) {
-  const LaunchPlan p = plan_act_quant(rows, K, false, compute_units());
-  // a block resolves its deferred rows with teams of K/32 lanes
-  if (p.block < K / 32 || p.block > 512) return hipErrorInvalidConfiguration;
+  // half rows are never deferred, so their blocks need not fit a K/32-lane row
+  const LaunchPlan p = f16 ? plan_rotate(rows, K / 64, kFastWavesPerCU, compute_units(), 1)
+                           : plan_act_quant(rows, K, false, compute_units());
+  // a bf16 block resolves its deferred rows with teams of K/32 lanes
+  if ((!f16 && p.block < K / 32) || p.block > 512) return hipErrorInvalidConfiguration;
   const int64_t nbatches = (rows + p.rows_per_block - 1) / p.rows_per_block;
   auto kern = f16 ? rotate_quant_fast_kernel<G, true> : rotate_quant_fast_kernel<G, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(p.block), 0, st, x, xq, s, rows, K,
@@ -1263,8 +1265,9 @@ hipError_t launch_exact(const uint16_t* x, int8_t* xq, float* s, uint32_t* tenso
 }  // namespace
 
 // The fast kernel's blocks hold at least two rows of K/64 lanes (K <= 16384),
-// so that one row of the exact pass's K/32 lanes fits a block. deferred: the
-// blocks' pass over the rows they defer, in the fast kernel's grid, with
+// so that one row of the exact pass's K/32 lanes fits a block (bf16 rows;
+// half rows, never deferred, take the shape without that floor). deferred:
+// the blocks' pass over the rows they defer, in the fast kernel's grid, with
 // rows_per_block rows of K/32 lanes per step.
 LaunchPlan plan_act_quant(int64_t rows, int K, bool deferred, int cus) {
   LaunchPlan p = plan_rotate(rows, K / 64, kFastWavesPerCU, cus, 2);

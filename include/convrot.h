@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define CONVROT_ABI_VERSION 6
+#define CONVROT_ABI_VERSION 7
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -330,7 +330,8 @@ convrot_status convrot_streamer_linear_int8(convrot_streamer* streamer, const vo
  * for a key, synchronously on `stream`:
  *   1. the first token slice is quantized and every GEMM tile that exists
  *      for k is timed on it (two runs each, after 256 MB - the MI355X MALL -
- *      have been written to the session's buffer); the fastest is kept;
+ *      have been written to the session's buffer); the fastest is kept (a
+ *      key given a tile by convrot_session_import skips this step);
  *   2. the forward runs with that tile and writes y;
  *   3. W_hat (convrot_dequant_derotate_ex in dtype) is formed in the
  *      session's buffer, a chunk of weight rows at a time, the first
@@ -363,6 +364,31 @@ convrot_status convrot_session_linear_int8(convrot_session* session, const void*
 convrot_status convrot_session_lookup(convrot_session* session, int64_t m, int64_t n, int64_t k,
                                       int g, convrot_dtype dtype, convrot_scale_mode scale_mode,
                                       int* tile, double* check_error, int* latched);
+
+/* The tuned tiles across processes (the tuning of a key's first call costs a
+ * dozen GEMM runs and cache flushes; a serving process can start from the
+ * last run's choices). For callers that keep a small table between runs.
+ *
+ * convrot_session_export: the session's table as text, host memory: the line
+ * "convrot-session-tiles 1", then one line per key, "n k bucket g dtype
+ * scale_mode tile" (decimal integers; bucket = ceil(log2 m); dtype and
+ * scale_mode the enum values), for every key with a first call and every
+ * imported key without one, in a fixed order. Writes at most buf_bytes
+ * bytes, NUL-terminated when buf_bytes > 0 (buf nullable when buf_bytes is
+ * 0) and returns the bytes the whole text needs, NUL included; 0 for a null
+ * session. Check errors are not exported.
+ *
+ * convrot_session_import: reads such text (host memory, NUL-terminated).
+ * Each line gives its key a tile: that key's first call then skips the
+ * timing and runs with the tile, and still runs the check against the
+ * default path (the same results: every tile gives the same bits). Keys that
+ * already had a first call keep their entry. The text must be well formed:
+ * the header line, seven integers per line with k % 64 == 0, k <= 16384,
+ * k % g == 0, g in {4, 16, 64, 256}, n % 16 == 0, a tile in {128, 192, 256,
+ * 384} that exists for k (384: k % 128 == 0); otherwise CONVROT_E_INVALID_ARG
+ * naming the line, and nothing is imported. Touches no GPU. */
+size_t convrot_session_export(convrot_session* session, char* buf, size_t buf_bytes);
+convrot_status convrot_session_import(convrot_session* session, const char* text);
 
 /* Workspace bytes that convrot_linear_int8 uses for slices of `rows` token rows. */
 size_t convrot_linear_int8_workspace_for_rows(int64_t rows, int64_t k);

@@ -27,6 +27,7 @@ __all__ = [
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
     "convrot_streamer_linear_int8", "Streamer", "convrot_session_create",
     "convrot_session_destroy", "convrot_session_linear_int8", "convrot_session_lookup",
+    "convrot_session_export", "convrot_session_import",
     "Session", "EXPORTED_SYMBOLS", "convrot_compute_units", "convrot_set_compute_units",
     "convrot_plan_launch", "KERNELS", "convrot_linear_int8_noalloc", "NOALLOC_SCRATCH_BYTES",
     "convrot_dequant_derotate_batched",
@@ -51,7 +52,8 @@ EXPORTED_SYMBOLS = (
     "convrot_quantize_activations_ex", "convrot_dequant_derotate_ex", "convrot_gemm_int8_ex",
     "convrot_linear_int8_ex", "convrot_streamer_create", "convrot_streamer_destroy",
     "convrot_streamer_linear_int8", "convrot_session_create", "convrot_session_destroy",
-    "convrot_session_linear_int8", "convrot_session_lookup", "convrot_compute_units",
+    "convrot_session_linear_int8", "convrot_session_lookup", "convrot_session_export",
+    "convrot_session_import", "convrot_compute_units",
     "convrot_set_compute_units", "convrot_plan_launch", "convrot_linear_int8_noalloc",
     "convrot_dequant_derotate_batched",
 )
@@ -137,6 +139,7 @@ def load_library():
                                             P],
             "convrot_session_lookup": [P, I64, I64, I64, I, I, I, ctypes.POINTER(I),
                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)],
+            "convrot_session_import": [P, ctypes.c_char_p],
             "convrot_set_compute_units": [I],
             "convrot_linear_int8_noalloc": [P, P, P, I, P, I64, I64, I64, I, U64, P, I, P],
             "convrot_dequant_derotate_batched": [ctypes.POINTER(_DequantJob), I, I, I, U64, I, P],
@@ -158,6 +161,8 @@ def load_library():
         lib.convrot_abi_version.restype = I
         lib.convrot_compute_units.argtypes = []
         lib.convrot_compute_units.restype = I
+        lib.convrot_session_export.argtypes = [P, ctypes.c_char_p, SZ]
+        lib.convrot_session_export.restype = SZ
         _lib = lib
         return lib
 
@@ -647,6 +652,24 @@ def convrot_session_lookup(session: ctypes.c_void_p, m: int, n: int, k: int, g: 
     return tile.value, err.value, bool(latched.value)
 
 
+def convrot_session_export(session: ctypes.c_void_p) -> str:
+    """The session's tuned tiles as text (one line per key), for
+    convrot_session_import in a later process."""
+    lib = load_library()
+    need = lib.convrot_session_export(session, None, 0)
+    if need == 0:
+        raise ConvrotError(1, lib.convrot_last_error_string().decode())
+    buf = ctypes.create_string_buffer(need)
+    lib.convrot_session_export(session, buf, need)
+    return buf.value.decode("ascii")
+
+
+def convrot_session_import(session: ctypes.c_void_p, text: str) -> None:
+    """Give the keys of exported text their tiles: their first calls skip the
+    timing (the check still runs). Malformed text raises, importing nothing."""
+    _check(load_library().convrot_session_import(session, text.encode("ascii")))
+
+
 class Session:
     """Owns a convrot_session: `with Session() as s: s.linear(...)`."""
 
@@ -658,6 +681,12 @@ class Session:
 
     def lookup(self, m, n, k, g, dtype=torch.bfloat16, per_channel=False):
         return convrot_session_lookup(self.handle, m, n, k, g, dtype, per_channel)
+
+    def export_tiles(self) -> str:
+        return convrot_session_export(self.handle)
+
+    def import_tiles(self, text: str) -> None:
+        convrot_session_import(self.handle, text)
 
     def close(self):
         if self.handle is not None:

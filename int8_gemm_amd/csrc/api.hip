@@ -822,6 +822,7 @@ struct convrot_session {
   bool latched = false;
   std::string latch_reason;
   std::map<SessionKey, SessionEntry> entries;
+  std::map<SessionKey, int> preset;  // imported tiles for keys without a first call
   std::mutex mu;
   void* scratch = nullptr;  // kSessionScratch bytes on `device`
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -866,18 +867,22 @@ static convrot_status session_first_call(const char* fn, convrot_session* s, boo
                                          const uint16_t* x, const int8_t* wq, const float* s_w,
                                          const uint16_t* bias, int64_t m, int64_t n, int64_t k,
                                          int g, uint64_t rot_seed, uint16_t* y, void* workspace,
-                                         int64_t slice, hipStream_t st, SessionEntry* entry) {
+                                         int64_t slice, hipStream_t st, int preset_tile,
+                                         SessionEntry* entry) {
   const SignMask sm = make_signs(rot_seed, g);
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                        align_up((size_t)(slice * k), 256));
   const int64_t rows0 = slice < m ? slice : m;
-  hipError_t e = launch_quantize_rows(x, xq, sx, rows0, (int)k, g, sm, dt, st);
+  hipError_t e = hipSuccess;
   // 1. time every tile that exists for k on the first slice, caches flushed
-  int best = 0;
+  // (an imported tile skips this)
+  int best = preset_tile;
   float best_ms = 0.0f;
+  if (best == 0) e = launch_quantize_rows(x, xq, sx, rows0, (int)k, g, sm, dt, st);
   const int cands[] = {384, 256, 192, 128};
   for (int c : cands) {
+    if (preset_tile != 0) break;
     if (e != hipSuccess) break;
     if (c == 384 && k % 128 != 0) continue;
     for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
@@ -968,8 +973,11 @@ convrot_status convrot_session_linear_int8(convrot_session* s, const void* x, co
     return linear_run(fn, pc, dt, xb, wq, s_w, bb, m, n, k, g, rot_seed, yb, workspace, slice,
                       stream, it->second.tile);
   SessionEntry entry{0, 0.0};
+  const auto pre = s->preset.find(key);
+  const int preset_tile = pre != s->preset.end() ? pre->second : 0;
   const convrot_status r = session_first_call(fn, s, pc, dt, xb, wq, s_w, bb, m, n, k, g, rot_seed,
-                                              yb, workspace, slice, (hipStream_t)stream, &entry);
+                                              yb, workspace, slice, (hipStream_t)stream,
+                                              preset_tile, &entry);
   char why[256];
   if (r != CONVROT_OK) {
     snprintf(why, sizeof why, "first call for n=%lld k=%lld failed: %s", (long long)n,
@@ -979,6 +987,7 @@ convrot_status convrot_session_linear_int8(convrot_session* s, const void* x, co
     return fail(CONVROT_E_SELFCHECK, "%s: %s", fn, why);
   }
   s->entries[key] = entry;
+  if (pre != s->preset.end()) s->preset.erase(pre);
   if (!(entry.err <= s->tol)) {
     snprintf(why, sizeof why,
              "first result for n=%lld k=%lld (token bucket 2^%d) is %.4g away from the default "
@@ -1007,6 +1016,76 @@ convrot_status convrot_session_lookup(convrot_session* s, int64_t m, int64_t n, 
   if (it == s->entries.end()) return fail(CONVROT_E_INVALID_ARG, "%s: no first call yet", fn);
   if (tile) *tile = it->second.tile;
   if (check_error) *check_error = it->second.err;
+  return ok();
+}
+
+static const char kTilesHeader[] = "convrot-session-tiles 1";
+
+size_t convrot_session_export(convrot_session* s, char* buf, size_t buf_bytes) {
+  if (!s) {
+    (void)fail(CONVROT_E_INVALID_ARG, "convrot_session_export: null session");
+    return 0;
+  }
+  std::string text = std::string(kTilesHeader) + "\n";
+  {
+    std::lock_guard<std::mutex> lock(s->mu);
+    std::map<SessionKey, int> all(s->preset);
+    for (const auto& kv : s->entries) all[kv.first] = kv.second.tile;
+    char line[160];
+    for (const auto& kv : all) {
+      const SessionKey& key = kv.first;
+      snprintf(line, sizeof line, "%lld %lld %d %d %d %d %d\n", (long long)std::get<0>(key),
+               (long long)std::get<1>(key), std::get<2>(key), std::get<3>(key), std::get<4>(key),
+               std::get<5>(key), kv.second);
+      text += line;
+    }
+  }
+  if (buf_bytes > 0 && buf) {
+    const size_t len = text.size() < buf_bytes - 1 ? text.size() : buf_bytes - 1;
+    memcpy(buf, text.data(), len);
+    buf[len] = '\0';
+  }
+  return text.size() + 1;
+}
+
+convrot_status convrot_session_import(convrot_session* s, const char* text) {
+  const char* fn = "convrot_session_import";
+  if (!s || !text) return fail(CONVROT_E_INVALID_ARG, "%s: null argument", fn);
+  std::map<SessionKey, int> got;
+  int lineno = 0;
+  const char* p = text;
+  while (*p) {
+    const char* eol = strchr(p, '\n');
+    const size_t len = eol ? (size_t)(eol - p) : strlen(p);
+    std::string line(p, len);
+    p += len + (eol ? 1 : 0);
+    ++lineno;
+    if (!line.empty() && line.back() == '\r') line.pop_back();
+    if (lineno == 1) {
+      if (line != kTilesHeader)
+        return fail(CONVROT_E_INVALID_ARG, "%s: line 1 is not \"%s\"", fn, kTilesHeader);
+      continue;
+    }
+    if (line.empty()) continue;
+    long long n = 0, k = 0;
+    int bucket = 0, g = 0, dtype = 0, mode = 0, tile = 0, used = 0;
+    const int got_fields = sscanf(line.c_str(), "%lld %lld %d %d %d %d %d %n", &n, &k, &bucket,
+                                  &g, &dtype, &mode, &tile, &used);
+    DType dt;
+    bool pc;
+    const bool ok_line =
+        got_fields == 7 && used == (int)line.size() && n >= 16 && n % 16 == 0 && k >= 64 &&
+        k % 64 == 0 && k <= kMaxRotK && (g == 4 || g == 16 || g == 64 || g == 256) &&
+        k % g == 0 && bucket >= 0 && bucket <= 62 && dtype_of(dtype, &dt) &&
+        scale_mode_of(mode, &pc) &&
+        (tile == 128 || tile == 192 || tile == 256 || (tile == 384 && k % 128 == 0));
+    if (!ok_line) return fail(CONVROT_E_INVALID_ARG, "%s: line %d is not a valid entry", fn, lineno);
+    got[SessionKey{(int64_t)n, (int64_t)k, bucket, g, (int)dt, pc ? 1 : 0}] = tile;
+  }
+  if (lineno == 0) return fail(CONVROT_E_INVALID_ARG, "%s: empty text", fn);
+  std::lock_guard<std::mutex> lock(s->mu);
+  for (const auto& kv : got)
+    if (s->entries.find(kv.first) == s->entries.end()) s->preset[kv.first] = kv.second;
   return ok();
 }
 

@@ -46,6 +46,11 @@ int convrot_header_c99_check(void* p, int i) {
                                     1, 16, 64, 4, 1u, p, p, 64, p);
     s = convrot_session_lookup(se, 1, 16, 64, 4, CONVROT_DTYPE_F16, CONVROT_SCALE_PER_CHANNEL,
                                &tile, &err, &latched);
+    {
+      char text[256];
+      tile += (int)convrot_session_export(se, text, sizeof text);
+      s = convrot_session_import(se, text);
+    }
     s = convrot_session_destroy(se);
     s = convrot_rotation_signs(1u, 4, q);
     (void)convrot_linear_int8_workspace_for_rows(1, 64);

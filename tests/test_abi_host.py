@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert cr.convrot_abi_version() == 6
+    assert cr.convrot_abi_version() == 7
     for s in range(8):
         assert cr.convrot_status_string(s)
     assert cr.convrot_status_string(7).startswith("first-call check")
@@ -252,6 +252,9 @@ def test_session_argument_checks_without_gpu(lib):
     t, e, lt = ctypes.c_int(), ctypes.c_double(), ctypes.c_int()
     assert lib.convrot_session_lookup(None, 8, 64, 256, 256, 0, 0, ctypes.byref(t),
                                       ctypes.byref(e), ctypes.byref(lt)) == 1
+    assert lib.convrot_session_export(None, None, 0) == 0
+    assert lib.convrot_session_import(None, b"convrot-session-tiles 1\n") == 1
+    assert lib.convrot_session_import(FAKE, None) == 1
 
 
 def test_header_compiles_and_links_as_c99(lib, tmp_path):

@@ -146,3 +146,61 @@ def test_check_over_column_chunks():
     want_err = oracle.rel_frobenius(y8, y_def)
     assert abs(err - want_err) <= 1e-4 + 1e-3 * want_err, (err, want_err)
     assert not latched and tile in TILES
+
+
+def test_tiles_exported_and_imported():
+    """A session's tuned tiles as text, read by another session: an imported
+    key's first call runs with the imported tile (a tile the timing would
+    not pick is kept as given) and still runs the check; its results equal
+    the plain forward's; the text of the second session lists the same keys;
+    malformed text imports nothing."""
+    cases = [(synth.ZIMAGE_ATTN.scaled(m=300, n=272), 256, False, torch.bfloat16),
+             (synth.QKV_SWEEP.scaled(m=260, n=288), 64, True, torch.float16)]
+    inputs = []
+    for layer, g, pc, dtype in cases:
+        fmt = "f16" if dtype == torch.float16 else "bf16"
+        wq_ref, s_ref = (oracle.quantize_weights_per_channel if pc else oracle.quantize_weights)(
+            layer.w(), g, SEED)
+        x = dev16(layer.x(fmt=fmt), dtype)
+        wq = torch.from_numpy(wq_ref).to(DEV)
+        s_w = torch.from_numpy(np.atleast_1d(s_ref).astype(np.float32)).to(DEV)
+        want = cr.convrot_linear_int8_ex(x, wq, s_w, g, SEED, per_channel=pc)
+        inputs.append((layer, g, pc, dtype, x, wq, s_w, want))
+    with cr.Session() as a:
+        for layer, g, pc, dtype, x, wq, s_w, want in inputs:
+            assert torch.equal(a.linear(x, wq, s_w, g, SEED, per_channel=pc).view(torch.int16),
+                               want.view(torch.int16))
+        text = a.export_tiles()
+        tiles_a = [a.lookup(l.m, l.n, l.k, g, dt, pc)[0] for l, g, pc, dt, *_ in inputs]
+    lines = text.splitlines()
+    assert lines[0] == "convrot-session-tiles 1" and len(lines) == 3
+    print("exported:", lines[1:], flush=True)
+    # the first key's tile replaced by one the timing did not keep
+    f = lines[1].split()
+    other = 128 if f[6] != "128" else 192
+    lines[1] = " ".join(f[:6] + [str(other)])
+    with cr.Session() as b:
+        b.import_tiles("\n".join(lines) + "\n")
+        with pytest.raises(cr.ConvrotError):     # imported, but no first call yet
+            b.lookup(inputs[0][0].m, inputs[0][0].n, inputs[0][0].k, inputs[0][1],
+                     inputs[0][3], inputs[0][2])
+        assert b.export_tiles() == "\n".join(lines) + "\n"
+        for i, (layer, g, pc, dtype, x, wq, s_w, want) in enumerate(inputs):
+            y = b.linear(x, wq, s_w, g, SEED, per_channel=pc)
+            assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+            tile, err, latched = b.lookup(layer.m, layer.n, layer.k, g, dtype, pc)
+            assert tile == (other if i == 0 else tiles_a[1]) and not latched
+            assert 0.0 < err < 0.05
+        # malformed text: nothing imported, entries unchanged
+        bad = ["", "convrot-session-tiles 2\n",
+               "convrot-session-tiles 1\n272 3840 9 256 0 0 384 7\n",
+               "convrot-session-tiles 1\n272 3840 9 256 0 0 320\n",
+               "convrot-session-tiles 1\n272 3904 9 64 0 0 384\n",   # 384 needs k % 128 == 0
+               "convrot-session-tiles 1\n270 3840 9 256 0 0 256\n",  # n % 16 != 0
+               "convrot-session-tiles 1\n272 3840 9 48 0 0 256\n",
+               "convrot-session-tiles 1\n272 3840 9 256 2 0 256\n"]
+        before = b.export_tiles()
+        for t in bad:
+            with pytest.raises(cr.ConvrotError):
+                b.import_tiles(t)
+        assert b.export_tiles() == before

@@ -428,7 +428,8 @@ typedef struct convrot_launch_plan {
   int64_t grid;           /* workgroups                                                  */
   int64_t passes;         /* persistent kernels: batches per workgroup (rounded up)      */
   int32_t block;          /* threads per workgroup                                       */
-  int32_t rows_per_block; /* act-quant: token rows per batch; dequant: 32-row tiles/step */
+  int32_t rows_per_block; /* act-quant: token rows per batch (its deferred rows: rows of
+                             K/32 lanes per step); dequant: 32-row tiles per step        */
   int32_t tile_m, tile_n; /* GEMM block tile (0 otherwise)                               */
   int32_t xcds;           /* XCDs of the GEMM's tile order                                */
   int32_t compute_units;  /* the CU count the plan was made for                          */

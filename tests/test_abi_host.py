@@ -309,6 +309,20 @@ def test_launch_plans_follow_compute_units(lib, cus):
     assert p["grid"] == -(-32760 // tm) * -(-13824 // tn)
 
 
+def test_act_quant_blocks_fit_a_deferred_row_at_every_k(lib):
+    """A fast-kernel block resolves the rows it defers with a team of K/32
+    lanes, so every bf16 act-quant block holds at least two K/64-lane rows;
+    the deferred-row plan runs in the same grid with whole K/32-lane rows."""
+    for cus in (256, 7):
+        for k in range(64, 16384 + 1, 64):
+            p = cr.convrot_plan_launch("act_quant", m=100000, k=k, g=4, compute_units=cus)
+            d = cr.convrot_plan_launch("act_quant_deferred", m=100000, k=k, g=4, compute_units=cus)
+            assert p["block"] % 64 == 0 and p["block"] <= 512, k
+            assert p["rows_per_block"] >= 2 and p["rows_per_block"] * (k // 64) <= p["block"], k
+            assert (d["grid"], d["block"], d["passes"]) == (p["grid"], p["block"], p["passes"]), k
+            assert d["rows_per_block"] == p["block"] // (k // 32) >= 1, k
+
+
 def test_gemm_tile_choice_counts_rounds_over_the_cus(lib):
     """The 384 x 192 tile covers 4608 x 3840 in 240 tiles, one round on 256
     CUs; on 128 CUs that takes two rounds, where the 256 x 256 tile's 270

@@ -195,3 +195,30 @@ def test_deferred_rows_past_the_pass_bitmap(few_cus):
     assert np.array_equal(f32_bits(sx_h[rows]), f32_bits(sx_ref))
     assert np.array_equal(xq.cpu().numpy()[rows], xq_ref)
     assert (sx_h[tiny] < 2.0 ** -100).all()
+
+
+@pytest.mark.parametrize("few_cus", [1], indirect=True)
+@pytest.mark.parametrize("g", [4, 16, 64, 256])
+def test_deferred_rows_every_group_size(few_cus, g):
+    """Always-deferred rows (elements near 2^-110) in many batches of a
+    one-CU grid, at every group size: the blocks resolve them after their
+    batches with the exact row pass of that g; those rows, the rows around
+    them and a sample of the rest against the oracle."""
+    k = 1024
+    plan = cr.convrot_plan_launch("act_quant", m=1 << 20, k=k, g=g)
+    grid, rpb = plan["grid"], plan["rows_per_block"]
+    m = grid * rpb * 40 + 3                      # a ragged last batch
+    print(f"deferred rows g={g}: grid {grid} rows/block {rpb} m {m}", flush=True)
+    rng = np.random.default_rng(100 + g)
+    xf = rng.standard_normal((m, k), dtype=np.float32)
+    tiny = np.unique(np.concatenate([rng.choice(m, 40, replace=False), [0, m - 1]]))
+    xf[tiny] *= np.float32(2.0 ** -110)
+    xb = synth.f32_to_bf16_bits(xf)
+    xq, sx = cr.convrot_quantize_activations(dev_bf16(xb), g, SEED)
+    sx_h = sx.cpu().numpy()
+    assert not np.isnan(sx_h).any()
+    near = np.clip(np.concatenate([tiny - 1, tiny + 1]), 0, m - 1)
+    rows = np.unique(np.concatenate([tiny, near, rng.choice(m, 500, replace=False)]))
+    xq_ref, sx_ref = oracle.quantize_activations(xb[rows], g, SEED)
+    assert np.array_equal(f32_bits(sx_h[rows]), f32_bits(sx_ref))
+    assert np.array_equal(xq.cpu().numpy()[rows], xq_ref)

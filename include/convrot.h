@@ -93,7 +93,7 @@ typedef enum convrot_status {
  * entry points). The pages' kernels run in BF16 and FP16 (Invoke docs "int8
  * Compute", the table of layers that keep unpacking). With FP16 every step is
  * the same; only the input decoding and the final rounding (to nearest even,
- * overflow to inf) change. IEEE half inputs never need the exact kernel:
+ * overflow to inf) change. IEEE half inputs never need the exact row pass:
  * each value is a multiple of 2^-24 below 2^16, so the float64 transform of a
  * group is exact. Non-finite inputs are out of contract for both formats. */
 typedef enum convrot_dtype { CONVROT_DTYPE_BF16 = 0, CONVROT_DTYPE_F16 = 1 } convrot_dtype;
@@ -175,8 +175,8 @@ convrot_status convrot_quantize_activations(const uint16_t* x, int64_t m, int64_
                                             void* stream);
 
 /* Test hook: the same result as convrot_quantize_activations, computed for every
- * row by the exact (banded) kernel that otherwise only finishes the rows whose
- * exponent span the fast kernel cannot sum exactly in float64. */
+ * row by the exact (banded) kernel, whose row pass otherwise only finishes,
+ * inside the fast kernel's launch, the rows that kernel cannot decide. */
 convrot_status convrot_quantize_activations_exact(const uint16_t* x, int64_t m, int64_t k, int g,
                                                   uint64_t rot_seed, int8_t* xq, float* s_x,
                                                   void* stream);

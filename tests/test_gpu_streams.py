@@ -26,7 +26,7 @@ def dev16(bits: np.ndarray, dtype=torch.bfloat16) -> torch.Tensor:
 
 
 def test_concurrent_streams_match_sequential():
-    # an ordinary layer, a GELU-tailed one (most rows take the deferred pass)
+    # an ordinary layer, a GELU-tailed one (some of its rows take the deferred pass)
     # with per-channel scales, and a half-precision one with g = 16
     specs = [(synth.ZIMAGE_ATTN.scaled(m=1000, n=512), 256, False, "bf16"),
              (synth.FLUX_MLP_DOWN.scaled(m=600, n=384), 256, True, "bf16"),
